@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Bench of the contextually sparse decode step on one MI355X.
+
+Workload: the OPT-175B-shaped stack of 24 decoder layers (d 12288, FFN 49152 ReLU,
+96 heads x 128, KV 2048 per layer, fp16 weights, predictor rank 1000), batch 1, 5 % of the
+neurons (2458) and 20 % of the heads (19) per layer, sets of layer l+1 predicted from the
+input of layer l on a side stream while layer l runs. Weights, caches and inputs are
+seeded synthetic draws generated in HBM (no trained weights exist here); x is fresh every
+step and residual-propagated through the stack.
+
+One step = one token through all 24 layers. Prints one JSON line:
+  value = us per sparse decode layer-token (lower is better), plus achieved HBM GB/s on the
+  step's algorithmic bytes, the roofline of the q/k/v gather kernel (timed live with HIP
+  events on its own stream), the dense layer through the same kernels and through torch,
+  and the CPU fp64 oracle timed on one layer-token of the same shape.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=24)
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--serial", action="store_true", help="run the predictor on the main stream")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path; see DESIGN.md for how the step would shard).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import contextual_activation_sparsity_amd as dv
+    from contextual_activation_sparsity_amd import _lib, traffic
+    import synth
+    import synth.device as sdev
+
+    dv.require_gpu()
+    w = synth.OPT175B_STACK.with_(n_layers=args.layers)
+    L = w.n_layers
+    dims = dv.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, w.t_max, w.dtype)
+    t0 = time.time()
+    layers, preds, kcs, vcs = [], [], [], []
+    for l in range(L):
+        t = sdev.layer_on_device(w, l)
+        layers.append(dv.LayerWeights(**{k: t[k] for k in ("g1", "g2", "wqkv", "bqkv", "wo", "bo", "w1t", "b1",
+                                                             "w2", "b2")}))
+        preds.append(dv.PredictorWeights(**{k: t[k] for k in ("p1_mlp", "p2_mlp", "p1_head", "p2_head")}))
+        kcs.append(sdev.kv_on_device(w, "k_cache", l))
+        vcs.append(sdev.kv_on_device(w, "v_cache", l))
+    n_steps = args.warmup + args.steps
+    xs = torch.empty(n_steps, 1, w.d_model, device="cuda")
+    for i in range(n_steps):
+        sdev.fill_(xs[i], w.key("x", 0, i), w.x_sigma)
+    y = torch.empty(1, w.d_model, device="cuda")
+    ws = dv.stack_workspace(dims, 1, w.k, w.kh)
+    side = None if args.serial else torch.cuda.Stream()
+    torch.cuda.synchronize()
+    log(f"[bench] {L} layers drawn in HBM in {time.time() - t0:.1f}s "
+        f"({torch.cuda.memory_allocated() / 1e9:.1f} GB allocated)")
+
+    def step(i):
+        dv.dv_lookahead_stack(dims, layers, preds, xs[i], w.k, w.kh, kcs, vcs, w.t_past, y, ws=ws,
+                              side_stream=side)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+
+    # Timed region: K steps; the q/k/v gather launches carry HIP event pairs on their stream.
+    n_ev = args.steps * L
+    assert _lib.lib().dv_timing_start(n_ev) == n_ev
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    h0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - h0
+    ms_total = ev0.elapsed_time(ev1)
+    import ctypes
+    qkv_ms = (ctypes.c_float * n_ev)()
+    got = _lib.lib().dv_timing_stop(qkv_ms, n_ev)
+    assert got == n_ev, f"timing hook recorded {got} of {n_ev}"
+    qkv_ms = np.array(qkv_ms[:n_ev], dtype=np.float64)
+    ms_per_step = ms_total / args.steps
+    us_per_layer = ms_per_step * 1e3 / L
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, {us_per_layer:.2f} us/layer-token "
+        f"(host wall {wall * 1e3 / args.steps:.3f} ms/step)")
+
+    tb = traffic.step_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.t_past, w.k, w.kh, 2)
+    step_bytes = tb["total"]
+    gbps = step_bytes / (us_per_layer * 1e-6) / 1e9
+    # q/k/v gather launch: weight rows + biases of the selected heads, input x, gains, q/k/v out
+    d, dh, kh = w.d_model, w.head_dim, w.kh
+    qkv_bytes = 3 * kh * dh * d * 2 + 3 * kh * dh * 4 + d * 4 + d * 4 + 3 * kh * dh * 4 + kh * 4
+    qkv_avg_us = float(np.mean(qkv_ms)) * 1e3
+    qkv_gbps = qkv_bytes / (qkv_avg_us * 1e-6) / 1e9
+
+    out = {
+        "metric": "µs per sparse decode layer-token + achieved HBM GB/s (% of peak), OPT-175B shape",
+        "value": round(us_per_layer, 3),
+        "unit": "us/layer-token",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "opt175b-shaped 24-layer sparse decode stack, lookahead predictor on a side stream",
+                   "layers": L, "d_model": w.d_model, "d_ffn": w.d_ffn, "n_heads": w.n_heads,
+                   "head_dim": w.head_dim, "kv_len": w.t_past, "rank": w.rank, "k": w.k, "kh": w.kh,
+                   "batch": 1, "storage": "f16 weights and KV, fp32 activations and accumulation",
+                   "side_stream": not args.serial},
+        "achieved_GBps": round(gbps, 1),
+        "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "bytes_per_layer_token": int(step_bytes),
+        "bytes_breakdown": {k: int(v) for k, v in tb.items()},
+        "roofline": {"bound": "hbm", "achieved": round(qkv_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(qkv_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "rowdot_kernel<f16,256,6,qkv> (head-sparse q/k/v gather-GEMV)",
+                     "bytes_per_launch": int(qkv_bytes), "avg_launch_us": round(qkv_avg_us, 3),
+                     "launches_timed": int(n_ev)},
+    }
+
+    if not args.no_dense:
+        out["dense"] = dense_baselines(dv, w, dims, layers, kcs, vcs, xs, args.dense_steps, log)
+        best = min(v["us_per_layer_token"] for v in out["dense"].values())
+        out["speedup_vs_dense"] = round(best / us_per_layer, 3)
+
+    del layers, preds, kcs, vcs, xs
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, log)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def dense_baselines(dv, w, dims, layers, kcs, vcs, xs, n_steps, log):
+    """The dense layer at the same shape: (a) the library's own gather kernels with every
+    neuron and head selected, (b) torch (hipBLASLt F.linear, matmul attention)."""
+    import torch
+    import torch.nn.functional as Fn
+    L = len(layers)
+    res = {}
+    idx = torch.arange(w.d_ffn, dtype=torch.int32, device="cuda")[None].contiguous()
+    heads = torch.arange(w.n_heads, dtype=torch.int32, device="cuda")[None].contiguous()
+    ws = dv.workspace(dims, 1, w.d_ffn, w.n_heads)
+    h = torch.empty(1, w.d_model, device="cuda")
+
+    def lib_step(x):
+        h.copy_(x)
+        for l in range(L):
+            dv.dv_layer_step(dims, layers[l], None, h, None, w.d_ffn, w.n_heads, idx, heads, kcs[l], vcs[l],
+                             w.t_past, h, ws=ws)
+
+    lib_step(xs[0])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_steps):
+        lib_step(xs[i])
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (n_steps * L)
+    res["library_all_selected"] = {"us_per_layer_token": round(us, 2)}
+    log(f"[bench] dense through the library: {us:.1f} us/layer-token")
+
+    H, dh, d, T = w.n_heads, w.head_dim, w.d_model, w.t_past
+
+    def torch_layer(x, lw, kc, vc):
+        xn = (x * torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + 1e-5) * lw.g1).half()
+        qkv = Fn.linear(xn, lw.wqkv.view(H * 3 * dh, d)).float().view(H, 3, dh) + lw.bqkv
+        q = (qkv[:, 0] / dh ** 0.5).half().unsqueeze(-1).contiguous()        # [H][dh][1]
+        K = kc[0, :, :T].contiguous()                                          # [H][T][dh]
+        V = vc[0, :, :T].contiguous()
+        s_past = torch.bmm(K, q).squeeze(-1).float()                           # [H][T]
+        s_cur = (qkv[:, 0] * qkv[:, 1]).sum(-1, keepdim=True) / dh ** 0.5
+        p = torch.softmax(torch.cat([s_past, s_cur], -1), -1)
+        o = torch.bmm(p[:, None, :T].half().contiguous(), V).squeeze(1).float() + p[:, T:] * qkv[:, 2]
+        return o
+
+    # Wo and W2 are stored with one row per input element; torch's dense form needs their
+    # transposes, made once here (outside the timed loop).
+    wo_t = [lw.wo.view(H * dh, d).t().contiguous() for lw in layers[:1]]
+    w2_t = [lw.w2.t().contiguous() for lw in layers[:1]]
+
+    def torch_full(x, l, lw, kc, vc):
+        o = torch_layer(x, lw, kc, vc)
+        h1 = x + Fn.linear(o.reshape(1, H * dh).half(), wo_t[0]).float() + lw.bo
+        xn2 = (h1 * torch.rsqrt(h1.pow(2).mean(-1, keepdim=True) + 1e-5) * lw.g2).half()
+        u = torch.relu(Fn.linear(xn2, lw.w1t).float() + lw.b1)
+        return h1 + Fn.linear(u.half(), w2_t[0]).float() + lw.b2
+
+    # torch baseline on layer 0 repeated (its transposed copies exist once); at 3.7 GB per
+    # layer nothing stays in cache between repeats.
+    reps = max(4, n_steps * 2)
+    x = xs[0].clone()
+    torch_full(x, 0, layers[0], kcs[0], vcs[0])
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch_full(x, 0, layers[0], kcs[0], vcs[0])
+    e1.record()
+    torch.cuda.synchronize()
+    us_t = e0.elapsed_time(e1) * 1e3 / reps
+    res["torch_dense_layer"] = {"us_per_layer_token": round(us_t, 2),
+                                "note": "F.linear (hipBLASLt) projections + bmm attention, fp16 storage"}
+    log(f"[bench] dense torch layer: {us_t:.1f} us/layer-token")
+    del wo_t, w2_t
+    return res
+
+
+def cpu_baseline(w, log):
+    """The fp64 oracle, as it stands, on one layer-token of the same shape: predictor over
+    all neurons and heads, exact top-k, then the dense-with-mask layer (every neuron's and
+    head's projection computed, masks applied). Weights drawn on the host (not timed)."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t0 = time.time()
+    t = synth.layer_tensors(w, 0)
+    kc = synth.kv_cache(w, "k_cache", 0)
+    vc = synth.kv_cache(w, "v_cache", 0)
+    x = synth.x_input(w, step=0)
+    log(f"[bench] oracle inputs drawn on the host in {time.time() - t0:.1f}s")
+    c0 = time.perf_counter()
+    s_m, s_h = oracle.predict(t["p1_mlp"], t["p2_mlp"], t["p1_head"], t["p2_head"], x)
+    S = oracle.topk(s_m.astype(np.float32), w.k)
+    Sh = oracle.topk(s_h.astype(np.float32), w.kh)
+    oracle.layer(x, t, kc, vc, w.t_past, S, Sh)
+    sec = time.perf_counter() - c0
+    log(f"[bench] oracle: one layer-token in {sec:.2f}s on {cores} threads")
+    return {"value": round(sec * 1e6, 1), "unit": "us/layer-token", "cores": int(cores), "kind": "oracle",
+            "sample": "one OPT-175B-shaped layer-token (layer 0, step 0): fp64 predictor + top-k + dense-with-mask "
+                      "layer over all 49152 neurons and 96 heads, KV 2048"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,200 @@
+"""Contextually sparse decoder-layer step on MI355X (gfx950): Python binding.
+
+The functions below carry the C ABI's names (include/dejavu_hip.h) and only marshal
+torch tensors (device memory) and the current HIP stream into the library. Every step of
+the layer runs in hand-written HIP kernels; there is no CPU or torch fallback.
+
+Typical use::
+
+    import contextual_activation_sparsity_amd as dv
+    dims = dv.Dims(d_model=4096, d_ffn=16384, n_heads=32, head_dim=128, rank_mlp=512,
+                   rank_head=512, t_max=2049, dtype="f16")
+    ws = dv.workspace(dims, B=1, k=820, kh=7)
+    dv.dv_layer_step(dims, layer, pred, x, x, 820, 7, None, None, kc, vc, 2048, x_out, ws=ws)
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Dict, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import DejavuError  # noqa: F401
+
+__all__ = ["Dims", "LayerWeights", "PredictorWeights", "workspace", "stack_workspace", "dv_predict",
+           "dv_topk", "dv_sparse_mlp", "dv_sparse_attn", "dv_layer_step", "dv_lookahead_stack",
+           "dv_workspace_bytes", "dv_stack_workspace_bytes", "require_gpu", "DejavuError"]
+
+_DT = {"f32": (_lib.DV_F32, torch.float32), "f16": (_lib.DV_F16, torch.float16)}
+
+
+@dataclasses.dataclass(frozen=True)
+class Dims:
+    d_model: int
+    d_ffn: int
+    n_heads: int
+    head_dim: int
+    rank_mlp: int
+    rank_head: int
+    t_max: int
+    dtype: str = "f16"
+
+    def c(self) -> _lib.DvDims:
+        return _lib.DvDims(self.d_model, self.d_ffn, self.n_heads, self.head_dim, self.rank_mlp,
+                           self.rank_head, self.t_max, _DT[self.dtype][0])
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _DT[self.dtype][1]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+@dataclasses.dataclass
+class LayerWeights:
+    """Device tensors of one layer (storage layouts as in include/dejavu_hip.h)."""
+    g1: torch.Tensor
+    g2: torch.Tensor
+    wqkv: torch.Tensor
+    bqkv: torch.Tensor
+    wo: torch.Tensor
+    bo: torch.Tensor
+    w1t: torch.Tensor
+    b1: torch.Tensor
+    w2: torch.Tensor
+    b2: torch.Tensor
+
+    def c(self) -> _lib.DvLayer:
+        return _lib.DvLayer(*[_ptr(getattr(self, f.name)) for f in dataclasses.fields(self)])
+
+
+@dataclasses.dataclass
+class PredictorWeights:
+    p1_mlp: torch.Tensor
+    p2_mlp: torch.Tensor
+    p1_head: torch.Tensor
+    p2_head: torch.Tensor
+
+    def c(self) -> _lib.DvPredictor:
+        return _lib.DvPredictor(*[_ptr(getattr(self, f.name)) for f in dataclasses.fields(self)])
+
+
+def require_gpu() -> None:
+    """Load the library and check that a GPU is visible; raise otherwise."""
+    _lib.lib()
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible: the sparse layer step runs only on the GPU")
+
+
+def dv_workspace_bytes(dims: Dims, B: int, k: int, kh: int) -> int:
+    d = dims.c()
+    return int(_lib.lib().dv_workspace_bytes(ctypes.byref(d), B, k, kh))
+
+
+def dv_stack_workspace_bytes(dims: Dims, B: int, k: int, kh: int) -> int:
+    d = dims.c()
+    return int(_lib.lib().dv_stack_workspace_bytes(ctypes.byref(d), B, k, kh))
+
+
+def _alloc_ws(n: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def workspace(dims: Dims, B: int, k: int, kh: int, device="cuda") -> torch.Tensor:
+    return _alloc_ws(dv_workspace_bytes(dims, B, k, kh), device)
+
+
+def stack_workspace(dims: Dims, B: int, k: int, kh: int, device="cuda") -> torch.Tensor:
+    return _alloc_ws(dv_stack_workspace_bytes(dims, B, k, kh), device)
+
+
+def _ws(ws: Optional[torch.Tensor]) -> Tuple[Optional[int], int]:
+    if ws is None:
+        return None, 0
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def dv_predict(dims: Dims, pred: PredictorWeights, x_pred: torch.Tensor, s_mlp: torch.Tensor,
+               s_head: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    d, p = dims.c(), pred.c()
+    wp, wn = _ws(ws)
+    st = _lib.lib().dv_predict(ctypes.byref(d), ctypes.byref(p), _ptr(x_pred), x_pred.shape[0], _ptr(s_mlp),
+                               _ptr(s_head), wp, wn, _stream(stream))
+    _lib.check("dv_predict", st)
+
+
+def dv_topk(scores: torch.Tensor, k: int, idx: torch.Tensor, ws: Optional[torch.Tensor] = None,
+            stream=None) -> None:
+    B, n = scores.shape
+    wp, wn = _ws(ws)
+    st = _lib.lib().dv_topk(_ptr(scores), B, n, k, _ptr(idx), wp, wn, _stream(stream))
+    _lib.check("dv_topk", st)
+
+
+def dv_sparse_mlp(dims: Dims, layer: LayerWeights, xn: torch.Tensor, idx: Optional[torch.Tensor], k: int,
+                  y: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    d, L = dims.c(), layer.c()
+    wp, wn = _ws(ws)
+    st = _lib.lib().dv_sparse_mlp(ctypes.byref(d), ctypes.byref(L), _ptr(xn), xn.shape[0], _ptr(idx), k,
+                                  _ptr(y), wp, wn, _stream(stream))
+    _lib.check("dv_sparse_mlp", st)
+
+
+def dv_sparse_attn(dims: Dims, layer: LayerWeights, xn: torch.Tensor, heads: Optional[torch.Tensor], kh: int,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, t_past: int, y: torch.Tensor,
+                   ws: torch.Tensor, stream=None) -> None:
+    d, L = dims.c(), layer.c()
+    wp, wn = _ws(ws)
+    st = _lib.lib().dv_sparse_attn(ctypes.byref(d), ctypes.byref(L), _ptr(xn), xn.shape[0], _ptr(heads), kh,
+                                   _ptr(k_cache), _ptr(v_cache), t_past, _ptr(y), wp, wn, _stream(stream))
+    _lib.check("dv_sparse_attn", st)
+
+
+def dv_layer_step(dims: Dims, layer: LayerWeights, pred: Optional[PredictorWeights], x: torch.Tensor,
+                  x_pred: Optional[torch.Tensor], k: int, kh: int, idx_in: Optional[torch.Tensor],
+                  heads_in: Optional[torch.Tensor], k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  t_past: int, x_out: torch.Tensor, idx_out: Optional[torch.Tensor] = None,
+                  heads_out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                  stream=None) -> None:
+    d, L = dims.c(), layer.c()
+    p = pred.c() if pred is not None else None
+    wp, wn = _ws(ws)
+    st = _lib.lib().dv_layer_step(ctypes.byref(d), ctypes.byref(L), ctypes.byref(p) if p is not None else None,
+                                  _ptr(x), _ptr(x_pred), x.shape[0], k, kh, _ptr(idx_in), _ptr(heads_in),
+                                  _ptr(k_cache), _ptr(v_cache), t_past, _ptr(x_out), _ptr(idx_out),
+                                  _ptr(heads_out), wp, wn, _stream(stream))
+    _lib.check("dv_layer_step", st)
+
+
+def dv_lookahead_stack(dims: Dims, layers: Sequence[LayerWeights], preds: Sequence[PredictorWeights],
+                       x: torch.Tensor, k: int, kh: int, k_caches: Sequence[torch.Tensor],
+                       v_caches: Sequence[torch.Tensor], t_past: int, y: torch.Tensor,
+                       h_all: Optional[torch.Tensor] = None, idx_out: Optional[torch.Tensor] = None,
+                       heads_out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                       stream=None, side_stream=None) -> None:
+    n = len(layers)
+    d = dims.c()
+    Ls = (_lib.DvLayer * n)(*[l.c() for l in layers])
+    Ps = (_lib.DvPredictor * n)(*[p.c() for p in preds])
+    kcs = (ctypes.c_void_p * n)(*[_ptr(t) for t in k_caches])
+    vcs = (ctypes.c_void_p * n)(*[_ptr(t) for t in v_caches])
+    wp, wn = _ws(ws)
+    main = _stream(stream)
+    side = main if side_stream is None else side_stream.cuda_stream
+    st = _lib.lib().dv_lookahead_stack(ctypes.byref(d), Ls, Ps, n, _ptr(x), x.shape[0], k, kh, kcs, vcs, t_past,
+                                       _ptr(y), _ptr(h_all), _ptr(idx_out), _ptr(heads_out), wp, wn, main, side)
+    _lib.check("dv_lookahead_stack", st)

@@ -1,0 +1,607 @@
+// C ABI of the sparse decoder-layer step: argument validation, workspace layout and the
+// launch sequence of each call. See include/dejavu_hip.h for the contract.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "dejavu_hip.h"
+#include "dv_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dv_status fail(dv_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+#define DV_HIP(call)                                                                      \
+  do {                                                                                    \
+    hipError_t e_ = (call);                                                               \
+    if (e_ != hipSuccess) return fail(DV_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define DV_TRY(expr)                 \
+  do {                               \
+    dv_status s_ = (expr);           \
+    if (s_ != DV_OK) return s_;      \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t align256(size_t x) { return (x + 255u) & ~size_t(255u); }
+
+struct DeviceInfo {
+  int cus = 0;
+  hipEvent_t ev_in = nullptr, ev_sel[2] = {nullptr, nullptr};
+};
+std::mutex g_mu;
+std::map<int, DeviceInfo> g_dev;
+
+dv_status device_info(DeviceInfo** out, bool events) {
+  int dev = 0;
+  DV_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_mu);
+  DeviceInfo& di = g_dev[dev];
+  if (di.cus == 0) {
+    int cus = 0;
+    DV_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    di.cus = cus > 0 ? cus : 1;
+  }
+  if (events && di.ev_in == nullptr) {
+    DV_HIP(hipEventCreateWithFlags(&di.ev_in, hipEventDisableTiming));
+    DV_HIP(hipEventCreateWithFlags(&di.ev_sel[0], hipEventDisableTiming));
+    DV_HIP(hipEventCreateWithFlags(&di.ev_sel[1], hipEventDisableTiming));
+  }
+  *out = &di;
+  return DV_OK;
+}
+
+bool is_f16(const dv_dims* d) { return d->dtype == DV_F16; }
+int vec_of(const dv_dims* d) { return is_f16(d) ? 8 : 4; }
+
+dv_status check_dims(const dv_dims* d) {
+  if (d == nullptr) return fail(DV_ERR_NULL, "dims is NULL");
+  if (d->dtype != DV_F32 && d->dtype != DV_F16) return fail(DV_ERR_DTYPE, "unknown dtype %d", d->dtype);
+  if (d->d_model <= 0 || d->d_ffn <= 0 || d->n_heads <= 0 || d->head_dim <= 0 || d->rank_mlp <= 0 ||
+      d->rank_head <= 0 || d->t_max <= 0)
+    return fail(DV_ERR_DIMS, "all dims must be positive");
+  if ((long long)d->n_heads * d->head_dim != d->d_model)
+    return fail(DV_ERR_DIMS, "d_model %d != n_heads %d * head_dim %d", d->d_model, d->n_heads, d->head_dim);
+  const int v = vec_of(d);
+  if (d->d_model % v || d->rank_mlp % v || d->rank_head % v)
+    return fail(DV_ERR_ALIGN, "d_model and ranks must be multiples of %d", v);
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(DV_ERR_DIMS, "head_dim must be 64 or 128");
+  int t, c;
+  if (!dv::rowdot_plan(d->d_model, is_f16(d), &t, &c)) return fail(DV_ERR_DIMS, "d_model %d unsupported", d->d_model);
+  if (!dv::rowdot_plan(d->rank_mlp, is_f16(d), &t, &c) || !dv::rowdot_plan(d->rank_head, is_f16(d), &t, &c))
+    return fail(DV_ERR_DIMS, "predictor rank unsupported");
+  if (d->d_ffn > 65536 || d->n_heads > 65536) return fail(DV_ERR_DIMS, "d_ffn and n_heads must be <= 65536");
+  return DV_OK;
+}
+
+dv_status check_k(const dv_dims* d, int B, int k, int kh) {
+  if (B <= 0) return fail(DV_ERR_DIMS, "batch must be positive");
+  if (k < 0 || k > d->d_ffn) return fail(DV_ERR_K, "k=%d outside [0, %d]", k, d->d_ffn);
+  if (kh < 0 || kh > d->n_heads) return fail(DV_ERR_K, "kh=%d outside [0, %d]", kh, d->n_heads);
+  return DV_OK;
+}
+
+dv_status check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(DV_ERR_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(DV_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  return DV_OK;
+}
+
+dv_status check_layer(const dv_layer* L, bool attn, bool mlp) {
+  if (L == nullptr) return fail(DV_ERR_NULL, "layer is NULL");
+  if (attn) {
+    DV_TRY(check_ptr(L->wqkv, "wqkv")); DV_TRY(check_ptr(L->bqkv, "bqkv"));
+    DV_TRY(check_ptr(L->wo, "wo")); DV_TRY(check_ptr(L->bo, "bo"));
+  }
+  if (mlp) {
+    DV_TRY(check_ptr(L->w1t, "w1t")); DV_TRY(check_ptr(L->b1, "b1"));
+    DV_TRY(check_ptr(L->w2, "w2")); DV_TRY(check_ptr(L->b2, "b2"));
+  }
+  return DV_OK;
+}
+
+dv_status check_pred(const dv_predictor* P) {
+  if (P == nullptr) return fail(DV_ERR_NULL, "predictor is NULL");
+  DV_TRY(check_ptr(P->p1_mlp, "p1_mlp")); DV_TRY(check_ptr(P->p2_mlp, "p2_mlp"));
+  DV_TRY(check_ptr(P->p1_head, "p1_head")); DV_TRY(check_ptr(P->p2_head, "p2_head"));
+  return DV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout (sized with the largest tiling any device can pick).
+// ---------------------------------------------------------------------------
+struct Layout {
+  size_t z, s_mlp, s_head, idx, heads, qkv, apart, o, h1, u, part, cnt, total;
+  int n_slices, max_chunks, n_cnt_attn, n_cnt_o, n_cnt_mlp;
+};
+
+Layout layout_of(const dv_dims* d, int B, int k, int kh) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
+  const size_t f = 4, Bz = (size_t)B;
+  const int v = vec_of(d);
+  const int tpk = d->head_dim / v;
+  const int kpp = 256 / tpk;
+  L.max_chunks = (d->t_max + 2 * kpp - 1) / (2 * kpp);
+  L.n_slices = (d->d_model + 64 * v - 1) / (64 * v);
+  L.z = take(f * Bz * (d->rank_mlp + d->rank_head));
+  L.s_mlp = take(f * Bz * d->d_ffn);
+  L.s_head = take(f * Bz * d->n_heads);
+  L.idx = take(f * Bz * k);
+  L.heads = take(f * Bz * kh);
+  L.qkv = take(f * Bz * kh * 3 * d->head_dim);
+  L.apart = take(f * Bz * kh * L.max_chunks * (d->head_dim + 2));
+  L.o = take(f * Bz * kh * d->head_dim);
+  L.h1 = take(f * Bz * d->d_model);
+  L.u = take(f * Bz * k);
+  L.part = take(f * Bz * dv::rowaxpy_max_rg() * d->d_model);
+  L.n_cnt_attn = B * kh;
+  L.n_cnt_o = B * L.n_slices;
+  L.n_cnt_mlp = B * L.n_slices;
+  L.cnt = take(f * (L.n_cnt_attn + L.n_cnt_o + L.n_cnt_mlp));
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+dv_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return DV_OK;
+  if (ws == nullptr) return fail(DV_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u) return fail(DV_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(DV_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", have, need);
+  return DV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Launch sequences (arguments already validated).
+// ---------------------------------------------------------------------------
+dv::RowDotSeg seg_of(const void* W, long long ld, int n_out, int G, int n_groups, const int32_t* idx,
+                     long long idx_bstride, const float* x, long long ldx, const float* norm_g,
+                     const float* bias, float* out, long long ldo, int relu) {
+  dv::RowDotSeg s{};
+  s.W = W; s.ld = ld; s.n_out = n_out; s.G = G; s.n_groups = n_groups; s.idx = idx;
+  s.idx_bstride = idx_bstride; s.x = x; s.ldx = ldx; s.norm_g = norm_g; s.bias = bias;
+  s.out = out; s.ldo = ldo; s.relu = relu; s.blocks = 0;
+  return s;
+}
+
+// Optional timing of the q/k/v projection launches (dv_timing_start / dv_timing_stop).
+struct TimingHook {
+  std::mutex mu;
+  std::vector<hipEvent_t> start, end;
+  int cursor = 0;
+  bool active = false;
+};
+TimingHook g_timing;
+
+dv_status run_rowdot(dv::RowDotArgs& a, bool f16, int B, int cus, hipStream_t st, int tag = 0) {
+  int tpr = 0, ch = 0;
+  if (!dv::rowdot_plan(a.d, f16, &tpr, &ch)) return fail(DV_ERR_DIMS, "row length %d unsupported", a.d);
+  for (int i = 0; i < a.nseg; ++i) a.seg[i].blocks = dv::rowdot_blocks_for(a.seg[i].n_out, tpr, ch, cus);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (tag == 1 && g_timing.active) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.active && g_timing.cursor < (int)g_timing.start.size()) {
+      e0 = g_timing.start[g_timing.cursor];
+      e1 = g_timing.end[g_timing.cursor];
+      ++g_timing.cursor;
+    }
+  }
+  if (e0) DV_HIP(hipEventRecord(e0, st));
+  DV_HIP(dv::launch_rowdot(a, f16, B, st, tag));
+  if (e1) DV_HIP(hipEventRecord(e1, st));
+  return DV_OK;
+}
+
+dv_status run_predict(const dv_dims* d, const dv_predictor* P, const float* x, int B, float* s_mlp,
+                      float* s_head, float* z, int cus, hipStream_t st) {
+  const bool f16 = is_f16(d);
+  const int rm = d->rank_mlp, rh = d->rank_head, D = d->d_model;
+  dv::RowDotArgs a{};
+  a.nseg = 2; a.d = D; a.eps = 0.f;
+  a.seg[0] = seg_of(P->p1_mlp, D, rm, 1, rm, nullptr, 0, x, D, nullptr, nullptr, z, rm + rh, 0);
+  a.seg[1] = seg_of(P->p1_head, D, rh, 1, rh, nullptr, 0, x, D, nullptr, nullptr, z + rm, rm + rh, 0);
+  DV_TRY(run_rowdot(a, f16, B, cus, st));
+  dv::RowDotSeg sm = seg_of(P->p2_mlp, rm, d->d_ffn, 1, d->d_ffn, nullptr, 0, z, rm + rh, nullptr, nullptr,
+                            s_mlp, d->d_ffn, 0);
+  dv::RowDotSeg sh = seg_of(P->p2_head, rh, d->n_heads, 1, d->n_heads, nullptr, 0, z + rm, rm + rh, nullptr,
+                            nullptr, s_head, d->n_heads, 0);
+  if (rm == rh) {
+    dv::RowDotArgs b{};
+    b.nseg = 2; b.d = rm; b.seg[0] = sm; b.seg[1] = sh;
+    DV_TRY(run_rowdot(b, f16, B, cus, st));
+  } else {
+    dv::RowDotArgs b{};
+    b.nseg = 1; b.d = rm; b.seg[0] = sm;
+    DV_TRY(run_rowdot(b, f16, B, cus, st));
+    dv::RowDotArgs c{};
+    c.nseg = 1; c.d = rh; c.seg[0] = sh;
+    DV_TRY(run_rowdot(c, f16, B, cus, st));
+  }
+  return DV_OK;
+}
+
+dv_status run_topk2(const float* s_mlp, int F, int k, int32_t* idx, const float* s_head, int H, int kh,
+                    int32_t* heads, int B, hipStream_t st) {
+  dv::TopkArgs t{};
+  t.nprob = 2;
+  t.p[0] = {s_mlp, F, k, idx};
+  t.p[1] = {s_head, H, kh, heads};
+  DV_HIP(dv::launch_topk(t, B, st));
+  return DV_OK;
+}
+
+// h_out = resid + (sum over selected heads of o_h . Wo_h + bo), x normalised with norm_g if given.
+dv_status run_attn(const dv_dims* d, const dv_layer* Lw, const float* x, const float* norm_g, int B,
+                   const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* y,
+                   const float* resid, const Layout& L, void* ws, int cus, hipStream_t st) {
+  const bool f16 = is_f16(d);
+  const int D = d->d_model, dh = d->head_dim, H = d->n_heads;
+  int* cnt = at<int>(ws, L.cnt);
+  float* qkv = at<float>(ws, L.qkv);
+  float* o = at<float>(ws, L.o);
+  if (kh > 0) {
+    dv::RowDotArgs a{};
+    a.nseg = 1; a.d = D; a.eps = 1e-5f;
+    a.clear_ptr = cnt; a.clear_n = L.n_cnt_attn + L.n_cnt_o;
+    a.seg[0] = seg_of(Lw->wqkv, D, kh * 3 * dh, 3 * dh, H, heads, kh, x, D, norm_g, Lw->bqkv, qkv,
+                      (long long)kh * 3 * dh, 0);
+    DV_TRY(run_rowdot(a, f16, B, cus, st, /*tag=*/1));
+    dv::AttnArgs at_{};
+    at_.qkv = qkv; at_.heads = heads; at_.kh = kh; at_.n_heads = H; at_.dh = dh; at_.t_past = t_past;
+    at_.t_max = d->t_max; at_.k_cache = kc; at_.v_cache = vc; at_.partial = at<float>(ws, L.apart);
+    at_.counters = cnt; at_.o = o;
+    if (!dv::attn_plan(dh, f16, t_past + 1, kh, B, cus, &at_.chunk, &at_.n_chunks))
+      return fail(DV_ERR_DIMS, "head_dim unsupported");
+    if (at_.n_chunks > L.max_chunks) return fail(DV_ERR_DIMS, "internal: attention chunk plan");
+    DV_HIP(dv::launch_attn(at_, f16, B, st));
+  }
+  dv::RowAxpyArgs r{};
+  int tpc = 0;
+  dv::rowaxpy_plan(D, kh * dh, f16, B, cus, &tpc, &r.n_slices, &r.RG);
+  r.W = Lw->wo; r.ld = D; r.d = D; r.n_rows = kh * dh; r.G = dh; r.n_groups = H; r.idx = heads;
+  r.idx_bstride = kh; r.coef = o; r.ldc = (long long)kh * dh; r.bias = Lw->bo; r.resid = resid; r.ldr = D;
+  r.out = y; r.ldo = D; r.partial = at<float>(ws, L.part); r.counters = cnt + L.n_cnt_attn;
+  DV_HIP(dv::launch_rowaxpy(r, f16, tpc, B, st));
+  return DV_OK;
+}
+
+dv_status run_mlp(const dv_dims* d, const dv_layer* Lw, const float* x, const float* norm_g, int B,
+                  const int32_t* idx, int k, float* y, const float* resid, const Layout& L, void* ws, int cus,
+                  hipStream_t st) {
+  const bool f16 = is_f16(d);
+  const int D = d->d_model, F = d->d_ffn;
+  int* cnt = at<int>(ws, L.cnt) + L.n_cnt_attn + L.n_cnt_o;
+  float* u = at<float>(ws, L.u);
+  if (k > 0) {
+    dv::RowDotArgs a{};
+    a.nseg = 1; a.d = D; a.eps = 1e-5f;
+    a.clear_ptr = cnt; a.clear_n = L.n_cnt_mlp;
+    a.seg[0] = seg_of(Lw->w1t, D, k, 1, F, idx, k, x, D, norm_g, Lw->b1, u, k, 1);
+    DV_TRY(run_rowdot(a, f16, B, cus, st));
+  }
+  dv::RowAxpyArgs r{};
+  int tpc = 0;
+  dv::rowaxpy_plan(D, k, f16, B, cus, &tpc, &r.n_slices, &r.RG);
+  r.W = Lw->w2; r.ld = D; r.d = D; r.n_rows = k; r.G = 1; r.n_groups = F; r.idx = idx; r.idx_bstride = k;
+  r.coef = u; r.ldc = k; r.bias = Lw->b2; r.resid = resid; r.ldr = D; r.out = y; r.ldo = D;
+  r.partial = at<float>(ws, L.part); r.counters = cnt;
+  DV_HIP(dv::launch_rowaxpy(r, f16, tpc, B, st));
+  return DV_OK;
+}
+
+dv_status run_layer(const dv_dims* d, const dv_layer* Lw, const float* x, int B, const int32_t* idx, int k,
+                    const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* x_out,
+                    const Layout& L, void* ws, int cus, hipStream_t st) {
+  float* h1 = at<float>(ws, L.h1);
+  DV_TRY(run_attn(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, t_past, h1, x, L, ws, cus, st));
+  DV_TRY(run_mlp(d, Lw, h1, Lw->g2, B, idx, k, x_out, h1, L, ws, cus, st));
+  return DV_OK;
+}
+
+dv_status check_layer_all(const dv_dims* d, const dv_layer* Lw) {
+  DV_TRY(check_layer(Lw, true, true));
+  DV_TRY(check_ptr(Lw->g1, "g1"));
+  DV_TRY(check_ptr(Lw->g2, "g2"));
+  (void)d;
+  return DV_OK;
+}
+
+dv_status check_kv(const dv_dims* d, void* kc, void* vc, int t_past) {
+  DV_TRY(check_ptr(kc, "k_cache"));
+  DV_TRY(check_ptr(vc, "v_cache"));
+  if (t_past < 0 || t_past + 1 > d->t_max)
+    return fail(DV_ERR_KV, "t_past=%d needs t_max >= t_past+1 (t_max=%d)", t_past, d->t_max);
+  return DV_OK;
+}
+
+}  // namespace
+
+// ===========================================================================
+// exported
+// ===========================================================================
+extern "C" {
+
+const char* dv_status_str(dv_status s) {
+  switch (s) {
+    case DV_OK: return "ok";
+    case DV_ERR_NULL: return "null pointer";
+    case DV_ERR_DIMS: return "bad dimensions";
+    case DV_ERR_K: return "k out of range";
+    case DV_ERR_DTYPE: return "bad dtype";
+    case DV_ERR_ALIGN: return "misaligned pointer or row length";
+    case DV_ERR_KV: return "kv cache position out of range";
+    case DV_ERR_WORKSPACE: return "workspace too small";
+    case DV_ERR_HIP: return "hip error";
+  }
+  return "unknown status";
+}
+
+const char* dv_last_error(void) { return g_err.c_str(); }
+
+const char* dv_version(void) { return "dejavu_hip 0.1 gfx950"; }
+
+int32_t dv_timing_start(int32_t n) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (g_timing.active || n <= 0) return -1;
+  g_timing.start.assign(n, nullptr);
+  g_timing.end.assign(n, nullptr);
+  for (int i = 0; i < n; ++i) {
+    if (hipEventCreate(&g_timing.start[i]) != hipSuccess || hipEventCreate(&g_timing.end[i]) != hipSuccess) {
+      for (auto e : g_timing.start) if (e) (void)hipEventDestroy(e);
+      for (auto e : g_timing.end) if (e) (void)hipEventDestroy(e);
+      g_timing.start.clear();
+      g_timing.end.clear();
+      fail(DV_ERR_HIP, "hipEventCreate failed");
+      return -1;
+    }
+  }
+  g_timing.cursor = 0;
+  g_timing.active = true;
+  return n;
+}
+
+int32_t dv_timing_stop(float* ms, int32_t n) {
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (!g_timing.active) return -1;
+  const int used = g_timing.cursor;
+  int rc = used;
+  for (int i = 0; i < used; ++i) {
+    float t = -1.f;
+    if (hipEventSynchronize(g_timing.end[i]) != hipSuccess ||
+        hipEventElapsedTime(&t, g_timing.start[i], g_timing.end[i]) != hipSuccess)
+      rc = -1;
+    if (ms != nullptr && i < n) ms[i] = t;
+  }
+  for (auto e : g_timing.start) (void)hipEventDestroy(e);
+  for (auto e : g_timing.end) (void)hipEventDestroy(e);
+  g_timing.start.clear();
+  g_timing.end.clear();
+  g_timing.cursor = 0;
+  g_timing.active = false;
+  return rc;
+}
+
+size_t dv_workspace_bytes(const dv_dims* dims, int32_t B, int32_t k, int32_t kh) {
+  if (check_dims(dims) != DV_OK || B <= 0 || k < 0 || kh < 0) return 0;
+  return layout_of(dims, B, k, kh).total;
+}
+
+size_t dv_stack_workspace_bytes(const dv_dims* dims, int32_t B, int32_t k, int32_t kh) {
+  if (check_dims(dims) != DV_OK || B <= 0 || k < 0 || kh < 0) return 0;
+  const Layout L = layout_of(dims, B, k, kh);
+  size_t off = align256(L.total);
+  off += align256(L.total);                                     // side-stream layout
+  off += 2 * align256(4 * (size_t)B * k) + 2 * align256(4 * (size_t)B * kh);  // set rings
+  off += 2 * align256(4 * (size_t)B * dims->d_model);           // residual ping-pong
+  return off;
+}
+
+dv_status dv_predict(const dv_dims* dims, const dv_predictor* pred, const float* x_pred, int32_t B,
+                     float* s_mlp, float* s_head, void* ws, size_t ws_bytes, hipStream_t stream) {
+  DV_TRY(check_dims(dims));
+  DV_TRY(check_pred(pred));
+  if (B <= 0) return fail(DV_ERR_DIMS, "batch must be positive");
+  DV_TRY(check_ptr(x_pred, "x_pred"));
+  DV_TRY(check_ptr(s_mlp, "s_mlp"));
+  DV_TRY(check_ptr(s_head, "s_head"));
+  const Layout L = layout_of(dims, B, 0, 0);
+  DV_TRY(check_ws(ws, ws_bytes, L.total));
+  DeviceInfo* di;
+  DV_TRY(device_info(&di, false));
+  return run_predict(dims, pred, x_pred, B, s_mlp, s_head, at<float>(ws, L.z), di->cus, stream);
+}
+
+dv_status dv_topk(const float* scores, int32_t B, int32_t n, int32_t k, int32_t* idx, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  (void)ws; (void)ws_bytes;
+  if (B <= 0 || n <= 0) return fail(DV_ERR_DIMS, "B and n must be positive");
+  if (n > 65536) return fail(DV_ERR_DIMS, "n must be <= 65536");
+  if (k < 0 || k > n) return fail(DV_ERR_K, "k=%d outside [0, %d]", k, n);
+  if (scores == nullptr) return fail(DV_ERR_NULL, "scores is NULL");
+  if (k > 0 && idx == nullptr) return fail(DV_ERR_NULL, "idx is NULL");
+  if (k == 0) return DV_OK;
+  dv::TopkArgs t{};
+  t.nprob = 1;
+  t.p[0] = {scores, n, k, idx};
+  t.p[1] = t.p[0];
+  DV_HIP(dv::launch_topk(t, B, stream));
+  return DV_OK;
+}
+
+dv_status dv_sparse_mlp(const dv_dims* dims, const dv_layer* layer, const float* xn, int32_t B,
+                        const int32_t* idx, int32_t k, float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  DV_TRY(check_dims(dims));
+  DV_TRY(check_layer(layer, false, true));
+  DV_TRY(check_k(dims, B, k, 0));
+  DV_TRY(check_ptr(xn, "xn"));
+  DV_TRY(check_ptr(y, "y"));
+  if (k > 0 && idx == nullptr) return fail(DV_ERR_NULL, "idx is NULL");
+  const Layout L = layout_of(dims, B, k, 0);
+  DV_TRY(check_ws(ws, ws_bytes, L.total));
+  DeviceInfo* di;
+  DV_TRY(device_info(&di, false));
+  return run_mlp(dims, layer, xn, nullptr, B, idx, k, y, nullptr, L, ws, di->cus, stream);
+}
+
+dv_status dv_sparse_attn(const dv_dims* dims, const dv_layer* layer, const float* xn, int32_t B,
+                         const int32_t* heads, int32_t kh, void* k_cache, void* v_cache, int32_t t_past,
+                         float* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  DV_TRY(check_dims(dims));
+  DV_TRY(check_layer(layer, true, false));
+  DV_TRY(check_k(dims, B, 0, kh));
+  DV_TRY(check_ptr(xn, "xn"));
+  DV_TRY(check_ptr(y, "y"));
+  DV_TRY(check_kv(dims, k_cache, v_cache, t_past));
+  if (kh > 0 && heads == nullptr) return fail(DV_ERR_NULL, "heads is NULL");
+  const Layout L = layout_of(dims, B, 0, kh);
+  DV_TRY(check_ws(ws, ws_bytes, L.total));
+  DeviceInfo* di;
+  DV_TRY(device_info(&di, false));
+  return run_attn(dims, layer, xn, nullptr, B, heads, kh, k_cache, v_cache, t_past, y, nullptr, L, ws,
+                  di->cus, stream);
+}
+
+dv_status dv_layer_step(const dv_dims* dims, const dv_layer* layer, const dv_predictor* pred, const float* x,
+                        const float* x_pred, int32_t B, int32_t k, int32_t kh, const int32_t* idx_in,
+                        const int32_t* heads_in, void* k_cache, void* v_cache, int32_t t_past, float* x_out,
+                        int32_t* idx_out, int32_t* heads_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  DV_TRY(check_dims(dims));
+  DV_TRY(check_layer_all(dims, layer));
+  DV_TRY(check_k(dims, B, k, kh));
+  DV_TRY(check_ptr(x, "x"));
+  DV_TRY(check_ptr(x_out, "x_out"));
+  DV_TRY(check_kv(dims, k_cache, v_cache, t_past));
+  const bool inline_pred = (idx_in == nullptr && heads_in == nullptr);
+  if (!inline_pred && (idx_in == nullptr || heads_in == nullptr))
+    return fail(DV_ERR_NULL, "give both idx_in and heads_in, or neither");
+  if (inline_pred) {
+    DV_TRY(check_pred(pred));
+    DV_TRY(check_ptr(x_pred, "x_pred"));
+  }
+  const Layout L = layout_of(dims, B, k, kh);
+  DV_TRY(check_ws(ws, ws_bytes, L.total));
+  DeviceInfo* di;
+  DV_TRY(device_info(&di, false));
+  const int32_t* idx = idx_in;
+  const int32_t* heads = heads_in;
+  if (inline_pred) {
+    int32_t* io = idx_out ? idx_out : at<int32_t>(ws, L.idx);
+    int32_t* ho = heads_out ? heads_out : at<int32_t>(ws, L.heads);
+    DV_TRY(run_predict(dims, pred, x_pred, B, at<float>(ws, L.s_mlp), at<float>(ws, L.s_head),
+                       at<float>(ws, L.z), di->cus, stream));
+    DV_TRY(run_topk2(at<float>(ws, L.s_mlp), dims->d_ffn, k, io, at<float>(ws, L.s_head), dims->n_heads, kh,
+                     ho, B, stream));
+    idx = io;
+    heads = ho;
+  } else {
+    if (idx_out && k > 0)
+      DV_HIP(hipMemcpyAsync(idx_out, idx_in, sizeof(int32_t) * B * k, hipMemcpyDeviceToDevice, stream));
+    if (heads_out && kh > 0)
+      DV_HIP(hipMemcpyAsync(heads_out, heads_in, sizeof(int32_t) * B * kh, hipMemcpyDeviceToDevice, stream));
+  }
+  return run_layer(dims, layer, x, B, idx, k, heads, kh, k_cache, v_cache, t_past, x_out, L, ws, di->cus,
+                   stream);
+}
+
+dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const dv_predictor* preds,
+                             int32_t n_layers, const float* x, int32_t B, int32_t k, int32_t kh,
+                             void* const* k_caches, void* const* v_caches, int32_t t_past, float* y, float* h_all,
+                             int32_t* idx_out, int32_t* heads_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                             hipStream_t side_stream) {
+  DV_TRY(check_dims(dims));
+  if (layers == nullptr || preds == nullptr || k_caches == nullptr || v_caches == nullptr)
+    return fail(DV_ERR_NULL, "layers, preds and cache arrays must be given");
+  if (n_layers <= 0) return fail(DV_ERR_DIMS, "n_layers must be positive");
+  DV_TRY(check_k(dims, B, k, kh));
+  DV_TRY(check_ptr(x, "x"));
+  DV_TRY(check_ptr(y, "y"));
+  if (h_all != nullptr) DV_TRY(check_ptr(h_all, "h_all"));
+  for (int l = 0; l < n_layers; ++l) {
+    DV_TRY(check_layer_all(dims, &layers[l]));
+    DV_TRY(check_pred(&preds[l]));
+    DV_TRY(check_kv(dims, k_caches[l], v_caches[l], t_past));
+  }
+  const Layout L = layout_of(dims, B, k, kh);
+  const size_t need = dv_stack_workspace_bytes(dims, B, k, kh);
+  DV_TRY(check_ws(ws, ws_bytes, need));
+  DeviceInfo* di;
+  DV_TRY(device_info(&di, true));
+  const int cus = di->cus;
+  const int D = dims->d_model;
+
+  // carve: main layout, side layout, set rings, residual ping-pong
+  size_t off = align256(L.total);
+  void* ws_side = static_cast<char*>(ws) + off;
+  off += align256(L.total);
+  int32_t* ring_idx[2];
+  int32_t* ring_heads[2];
+  for (int i = 0; i < 2; ++i) { ring_idx[i] = at<int32_t>(ws, off); off += align256(4 * (size_t)B * k); }
+  for (int i = 0; i < 2; ++i) { ring_heads[i] = at<int32_t>(ws, off); off += align256(4 * (size_t)B * kh); }
+  float* pp[2];
+  for (int i = 0; i < 2; ++i) { pp[i] = at<float>(ws, off); off += align256(4 * (size_t)B * D); }
+
+  const size_t vecb = sizeof(float) * (size_t)B * D;
+  auto h_in = [&](int l) -> const float* {
+    if (h_all) return h_all + (size_t)l * B * D;
+    return l == 0 ? x : pp[l % 2];
+  };
+  auto h_outp = [&](int l) -> float* {
+    if (h_all) return h_all + (size_t)(l + 1) * B * D;
+    return l == n_layers - 1 ? y : pp[(l + 1) % 2];
+  };
+  auto sel_idx = [&](int l) -> int32_t* { return idx_out ? idx_out + (size_t)l * B * k : ring_idx[l % 2]; };
+  auto sel_heads = [&](int l) -> int32_t* {
+    return heads_out ? heads_out + (size_t)l * B * kh : ring_heads[l % 2];
+  };
+  auto predict_sets = [&](int l, const float* hin, void* w, hipStream_t st) -> dv_status {
+    DV_TRY(run_predict(dims, &preds[l], hin, B, at<float>(w, L.s_mlp), at<float>(w, L.s_head), at<float>(w, L.z),
+                       cus, st));
+    return run_topk2(at<float>(w, L.s_mlp), dims->d_ffn, k, sel_idx(l), at<float>(w, L.s_head), dims->n_heads,
+                     kh, sel_heads(l), B, st);
+  };
+
+  const bool two = side_stream != stream;
+  if (h_all) DV_HIP(hipMemcpyAsync(h_all, x, vecb, hipMemcpyDeviceToDevice, stream));
+  // Layer 0's sets come from the stack input, before any layer runs.
+  DV_TRY(predict_sets(0, h_in(0), ws, stream));
+  for (int l = 0; l < n_layers; ++l) {
+    if (l + 1 < n_layers) {
+      // Sets of layer l+1 from the input of layer l, overlapping layer l.
+      if (two) {
+        DV_HIP(hipEventRecord(di->ev_in, stream));
+        DV_HIP(hipStreamWaitEvent(side_stream, di->ev_in, 0));
+        DV_TRY(predict_sets(l + 1, h_in(l), ws_side, side_stream));
+        DV_HIP(hipEventRecord(di->ev_sel[(l + 1) % 2], side_stream));
+      } else {
+        DV_TRY(predict_sets(l + 1, h_in(l), ws_side, stream));
+      }
+    }
+    if (two && l >= 1) DV_HIP(hipStreamWaitEvent(stream, di->ev_sel[l % 2], 0));
+    DV_TRY(run_layer(dims, &layers[l], h_in(l), B, sel_idx(l), k, sel_heads(l), kh, k_caches[l], v_caches[l],
+                     t_past, h_outp(l), L, ws, cus, stream));
+  }
+  if (h_all && y != h_all + (size_t)n_layers * B * D)
+    DV_HIP(hipMemcpyAsync(y, h_all + (size_t)n_layers * B * D, vecb, hipMemcpyDeviceToDevice, stream));
+  return DV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Internal launch interface between the C ABI (dv_api.hip) and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dv {
+
+// ---------------------------------------------------------------------------
+// Gather row-dot ("GEMV1"): out[b][i] = act(dot(W[row_b(i)], xhat_b) + bias[row_b(i)])
+//   row_b(i) = grp * G + (i % G), grp = idx ? idx[b*idx_bstride + i/G] : i/G.
+//   xhat_b = norm_g ? norm_g * x_b / sqrt(mean(x_b^2) + eps) : x_b.
+// A group id outside [0, n_groups) yields 0 and is never dereferenced.
+// ---------------------------------------------------------------------------
+struct RowDotSeg {
+  const void* W;
+  long long ld;             // row stride (elements)
+  int n_out;                // outputs per batch row
+  int G;                    // consecutive rows per selected group
+  int n_groups;
+  const int32_t* idx;       // nullable -> identity
+  long long idx_bstride;
+  const float* x;           // [B][ldx]
+  long long ldx;
+  const float* norm_g;      // nullable -> no norm
+  const float* bias;        // nullable
+  float* out;               // [B][ldo]
+  long long ldo;
+  int relu;
+  int blocks;               // blocks (grid.x) given to this segment
+};
+
+struct RowDotArgs {
+  RowDotSeg seg[2];
+  int nseg;
+  int d;                    // row length (elements), shared by both segments
+  float eps;
+  int* clear_ptr;           // block (0,0) zeroes clear_n ints (counters of later kernels)
+  int clear_n;
+};
+
+// Chooses the tiling for row length d (elements) and storage type; returns false if d is
+// not supported. rows_in_flight: rows one block keeps loading at once.
+bool rowdot_plan(int d, bool f16, int* tpr, int* ch);
+int rowdot_blocks_for(int n_out, int tpr, int ch, int cus);
+hipError_t launch_rowdot(const RowDotArgs& a, bool f16, int B, hipStream_t s, int tag);
+
+// ---------------------------------------------------------------------------
+// Gather row-axpy ("GEMV2"): out[b][c] = sum_i coef[b][i] * W[row_b(i)][c] + bias[c] + resid[b][c]
+//   Split over column slices (grid.x) and row groups (grid.y); row-group partials are summed
+//   in a fixed order by the last block of each slice (deterministic).
+// ---------------------------------------------------------------------------
+struct RowAxpyArgs {
+  const void* W;
+  long long ld;
+  int d;
+  int n_rows;               // rows per batch row
+  int G;
+  int n_groups;
+  const int32_t* idx;
+  long long idx_bstride;
+  const float* coef;        // [B][ldc]
+  long long ldc;
+  const float* bias;        // [d] nullable
+  const float* resid;       // [B][ldr] nullable
+  long long ldr;
+  float* out;               // [B][ldo]
+  long long ldo;
+  float* partial;           // [B][RG][d]
+  int* counters;            // [B][n_slices], zero on entry; left zero on exit
+  int RG;
+  int n_slices;
+};
+
+void rowaxpy_plan(int d, int n_rows, bool f16, int B, int cus, int* tpc, int* n_slices, int* RG);
+int rowaxpy_max_rg();
+hipError_t launch_rowaxpy(const RowAxpyArgs& a, bool f16, int tpc, int B, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Head-sparse decode attention with split-T partials and in-kernel combine.
+// ---------------------------------------------------------------------------
+struct AttnArgs {
+  const float* qkv;         // [B][kh][3][dh] fp32 (q, k, v of each selected head)
+  const int32_t* heads;     // [B][kh]
+  int kh;
+  int n_heads;
+  int dh;
+  int t_past;
+  int t_max;
+  void* k_cache;            // [B][H][t_max][dh]
+  void* v_cache;
+  int chunk;                // keys per block
+  int n_chunks;
+  float* partial;           // [B][kh][n_chunks][dh + 2]
+  int* counters;            // [B][kh]
+  float* o;                 // [B][kh][dh]
+};
+bool attn_plan(int dh, bool f16, int t_total, int kh, int B, int cus, int* chunk, int* n_chunks);
+hipError_t launch_attn(const AttnArgs& a, bool f16, int B, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Exact top-k by radix select (one block per row and problem).
+// ---------------------------------------------------------------------------
+struct TopkProb {
+  const float* scores;      // [B][n]
+  int n;
+  int k;
+  int32_t* out;             // [B][k]
+};
+struct TopkArgs {
+  TopkProb p[2];
+  int nprob;
+};
+hipError_t launch_topk(const TopkArgs& a, int B, hipStream_t s);
+
+}  // namespace dv

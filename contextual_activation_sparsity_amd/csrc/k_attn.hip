@@ -1,0 +1,215 @@
+// Head-sparse decode attention (DejaVu Guide, "Head-Pruned Attention Dispatch").
+//
+// Only the selected heads are visited: a block handles one (batch row, selected head,
+// chunk of key positions). Positions 0..t_past-1 come from the head's cache region
+// [t_max][dh] (head-major, so a selected head reads one contiguous span); position t_past
+// is the current token, whose k and v come from the fp32 projection and are appended to
+// the cache (rounded to the storage type) by the block that owns that position.
+//
+// Per block: scores s_t = q.K_t / sqrt(dh) with TPK = dh/VEC threads per key (a 16-byte
+// chunk each, summed by an xor butterfly), the chunk maximum m, p_t = exp(s_t - m), the
+// unnormalised p.V in fp32 and l = sum p. Partials (m, l, o) go to the workspace; the last
+// block of each head (device-scope counter) rescales and sums them in chunk order and
+// writes o_h = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M). Deterministic.
+#include "dv_device.h"
+#include "dv_kernels.h"
+
+namespace dv {
+
+constexpr int kAttnBlock = 256;
+
+template <typename WT, int DH, int NPASS>
+__global__ __launch_bounds__(kAttnBlock) void attn_kernel(AttnArgs a) {
+  constexpr int VEC = Vec<WT>::N;
+  constexpr int TPK = DH / VEC;
+  constexpr int KPP = kAttnBlock / TPK;
+  constexpr int TC = KPP * NPASS;
+  constexpr int NW = kAttnBlock / kWave;
+  static_assert(TPK <= kWave, "one key per wave at most");
+  __shared__ float s_o[KPP][DH];
+  __shared__ float s_l[KPP];
+  __shared__ float s_m[NW];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int ks = tid / TPK;
+  const int kl = tid % TPK;
+  const int c = blockIdx.x;
+  const int s = blockIdx.y;
+  const int b = blockIdx.z;
+  const int h = a.heads[(long long)b * a.kh + s];
+  const bool hv = (unsigned)h < (unsigned)a.n_heads;
+  const int t_past = a.t_past;
+  const float LOG2E = 1.4426950408889634f;
+
+  const float* qkv = a.qkv + ((long long)b * a.kh + s) * 3 * DH;
+  float q[VEC], kcur[VEC], vcur[VEC];
+  const float qscale = LOG2E / sqrtf((float)DH);
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    q[e] = qkv[kl * VEC + e] * qscale;
+    kcur[e] = qkv[DH + kl * VEC + e];
+    vcur[e] = qkv[2 * DH + kl * VEC + e];
+  }
+
+  const long long hoff = hv ? (((long long)b * a.n_heads + h) * a.t_max) * DH : 0;
+  WT* K = reinterpret_cast<WT*>(a.k_cache) + hoff;
+  WT* V = reinterpret_cast<WT*>(a.v_cache) + hoff;
+  const int t0 = c * TC;
+
+  Chunk<WT> kc[NPASS], vc[NPASS];
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int t = t0 + p * KPP + ks;
+    if (hv && t < t_past) {
+      kc[p] = load_chunk<WT>(K + (long long)t * DH + kl * VEC);
+      vc[p] = load_chunk<WT>(V + (long long)t * DH + kl * VEC);
+    } else {
+      kc[p].raw = u32x4{0u, 0u, 0u, 0u};
+      vc[p].raw = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // Scores (log2 domain) and the block maximum.
+  float sc[NPASS];
+  float m = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < NPASS; ++p) {
+    const int t = t0 + p * KPP + ks;
+    float kf[VEC];
+    if (t < t_past) widen(kc[p], kf);
+    else
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) kf[e] = kcur[e];
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dot = fmaf(q[e], kf[e], dot);
+    dot = group_sum<TPK>(dot);
+    sc[p] = (hv && t <= t_past) ? dot : -INFINITY;
+    m = fmaxf(m, sc[p]);
+  }
+  m = group_max<kWave>(m);
+  if ((tid % kWave) == 0) s_m[tid / kWave] = m;
+  __syncthreads();
+  m = s_m[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, s_m[w]);
+
+  // p . V and sum p (only chunks with at least one valid key reach a finite m).
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  float l = 0.f;
+  if (m > -INFINITY) {
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const int t = t0 + p * KPP + ks;
+      const float pw = (sc[p] > -INFINITY) ? exp2f(sc[p] - m) : 0.f;
+      float vf[VEC];
+      if (t < t_past) widen(vc[p], vf);
+      else
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) vf[e] = (t == t_past) ? vcur[e] : 0.f;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = fmaf(pw, vf[e], acc[e]);
+      l += pw;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s_o[ks][kl * VEC + e] = acc[e];
+  if (kl == 0) s_l[ks] = l;
+
+  // Append the current token's k, v to the cache of this head.
+  if (hv && t_past >= t0 && t_past < t0 + TC) {
+    const int own = (t_past - t0) % KPP;  // key slot that met position t_past
+    if (ks == own) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        K[(long long)t_past * DH + kl * VEC + e] = narrow<WT>(kcur[e]);
+        V[(long long)t_past * DH + kl * VEC + e] = narrow<WT>(vcur[e]);
+      }
+    }
+  }
+  __syncthreads();
+
+  float* part = a.partial + (((long long)b * a.kh + s) * a.n_chunks + c) * (DH + 2);
+  for (int e = tid; e < DH; e += kAttnBlock) {
+    float v = 0.f;
+#pragma unroll
+    for (int r = 0; r < KPP; ++r) v += s_o[r][e];
+    part[2 + e] = v;
+  }
+  if (tid == 0) {
+    float lt = 0.f;
+#pragma unroll
+    for (int r = 0; r < KPP; ++r) lt += s_l[r];
+    part[0] = m;
+    part[1] = lt;
+  }
+
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    const int prev = atomicAdd(&a.counters[b * a.kh + s], 1);
+    s_last = (prev == a.n_chunks - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  const float* base = a.partial + ((long long)b * a.kh + s) * a.n_chunks * (DH + 2);
+  float M = -INFINITY;
+  for (int cc = 0; cc < a.n_chunks; ++cc) M = fmaxf(M, base[cc * (DH + 2)]);
+  float* o = a.o + ((long long)b * a.kh + s) * DH;
+  for (int e = tid; e < DH; e += kAttnBlock) {
+    float L = 0.f, O = 0.f;
+    if (M > -INFINITY) {
+      for (int cc = 0; cc < a.n_chunks; ++cc) {
+        const float mc = base[cc * (DH + 2)];
+        const float f = (mc > -INFINITY) ? exp2f(mc - M) : 0.f;
+        L = fmaf(base[cc * (DH + 2) + 1], f, L);
+        O = fmaf(base[cc * (DH + 2) + 2 + e], f, O);
+      }
+    }
+    o[e] = (L > 0.f) ? O / L : 0.f;
+  }
+  if (tid == 0) a.counters[b * a.kh + s] = 0;
+}
+
+bool attn_plan(int dh, bool f16, int t_total, int kh, int B, int cus, int* chunk, int* n_chunks) {
+  const int vec = f16 ? 8 : 4;
+  if (dh != 64 && dh != 128) return false;
+  const int tpk = dh / vec;
+  const int kpp = kAttnBlock / tpk;
+  const long long want = 2LL * cus;
+  int npass = 2;
+  for (int np : {8, 4}) {
+    const long long nc = (t_total + kpp * np - 1) / (kpp * np);
+    if (nc * kh * B >= want) { npass = np; break; }
+  }
+  *chunk = kpp * npass;
+  *n_chunks = (t_total + *chunk - 1) / *chunk;
+  return true;
+}
+
+template <typename WT, int DH>
+static hipError_t launch_dh(const AttnArgs& a, int B, hipStream_t s) {
+  constexpr int VEC = Vec<WT>::N;
+  constexpr int KPP = kAttnBlock / (DH / VEC);
+  dim3 grid(a.n_chunks, a.kh, B);
+  switch (a.chunk / KPP) {
+    case 2: hipLaunchKernelGGL((attn_kernel<WT, DH, 2>), grid, dim3(kAttnBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((attn_kernel<WT, DH, 4>), grid, dim3(kAttnBlock), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((attn_kernel<WT, DH, 8>), grid, dim3(kAttnBlock), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnArgs& a, bool f16, int B, hipStream_t s) {
+  if (a.kh == 0) return hipSuccess;
+  if (f16) return a.dh == 128 ? launch_dh<half_t, 128>(a, B, s) : launch_dh<half_t, 64>(a, B, s);
+  return a.dh == 128 ? launch_dh<float, 128>(a, B, s) : launch_dh<float, 64>(a, B, s);
+}
+
+}  // namespace dv

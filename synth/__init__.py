@@ -80,7 +80,12 @@ def stream_key(seed: int, workload: int, layer: int, tensor: int, step: int = 0)
 
 def raw_bits(key: int, start: int, count: int) -> np.ndarray:
     """Outputs ``start .. start+count-1`` of the SplitMix64 stream ``key``."""
-    ctr = np.arange(start + 1, start + count + 1, dtype=np.uint64)
+    return raw_bits_at(key, np.arange(start, start + count, dtype=np.uint64))
+
+
+def raw_bits_at(key: int, counters: np.ndarray) -> np.ndarray:
+    """Outputs of the SplitMix64 stream ``key`` at arbitrary (0-based) counters."""
+    ctr = np.asarray(counters, dtype=np.uint64) + np.uint64(1)
     with np.errstate(over="ignore"):
         z = np.uint64(key) + ctr * np.uint64(GOLDEN)
     return mix64(z)
@@ -93,11 +98,43 @@ def scale_f32(sigma: float) -> np.float32:
 
 def normal_f32(key: int, start: int, count: int, sigma: float) -> np.ndarray:
     """Near-Gaussian fp32 values (mean 0, std sigma) for counters start..start+count-1."""
-    b = raw_bits(key, start, count)
+    return normal_f32_at(key, np.arange(start, start + count, dtype=np.uint64), sigma)
+
+
+def _normal_chunk(key: int, ctr: np.ndarray, scale: np.float32, out: np.ndarray) -> None:
+    b = raw_bits_at(key, ctr)
     m = np.uint64(0xFFFF)
     s = (b & m) + ((b >> np.uint64(16)) & m) + ((b >> np.uint64(32)) & m) + (b >> np.uint64(48))
     z = s.astype(np.int64) - IH4_CENTER
-    return z.astype(np.float32) * scale_f32(sigma)
+    np.multiply(z.astype(np.float32), scale, out=out)
+
+
+_CHUNK = 1 << 16
+
+
+def normal_f32_at(key: int, counters: np.ndarray, sigma: float) -> np.ndarray:
+    """Near-Gaussian fp32 values at arbitrary counters.
+
+    Large requests are cut into cache-sized chunks spread over threads; every element
+    is computed by the same operations either way.
+    """
+    counters = np.asarray(counters, dtype=np.uint64).reshape(-1)
+    n = counters.size
+    out = np.empty(n, np.float32)
+    scale = scale_f32(sigma)
+    if n <= 4 * _CHUNK:
+        _normal_chunk(key, counters, scale, out)
+        return out
+    starts = range(0, n, _CHUNK)
+    with _pool() as ex:
+        list(ex.map(lambda a: _normal_chunk(key, counters[a:a + _CHUNK], scale, out[a:a + _CHUNK]), starts))
+    return out
+
+
+def _pool():
+    import concurrent.futures as cf
+    import os
+    return cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
 
 
 def uniform01(key: int, start: int, count: int) -> np.ndarray:
@@ -131,8 +168,12 @@ def rows(key: int, shape: Tuple[int, ...], sigma: float, dtype: str, row_ids) ->
     row_ids = np.asarray(row_ids, dtype=np.int64).reshape(-1)
     row = int(np.prod(shape[1:]))
     out = np.empty((row_ids.size, row), np_dtype(dtype))
-    for n, r in enumerate(row_ids):
-        out[n] = tensor(key, shape, sigma, dtype, int(r), 1).reshape(-1)
+    step = max(1, (1 << 22) // max(row, 1))
+    for a in range(0, row_ids.size, step):
+        r = row_ids[a:a + step]
+        ctr = (r[:, None] * row + np.arange(row, dtype=np.int64)[None, :]).astype(np.uint64)
+        vals = normal_f32_at(key, ctr.reshape(-1), sigma) if sigma != 0.0 else np.zeros(ctr.size, np.float32)
+        out[a:a + step] = vals.astype(np_dtype(dtype)).reshape(r.size, row)
     return out.reshape((row_ids.size,) + tuple(shape[1:]))
 
 
