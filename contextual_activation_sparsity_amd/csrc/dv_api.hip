@@ -126,8 +126,8 @@ dv_status check_pred(const dv_predictor* P) {
 // Workspace layout (sized with the largest tiling any device can pick).
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t z, s_mlp, s_head, idx, heads, qkv, apart, o, h1, u, part, cnt, total;
-  int n_slices, max_chunks, n_cnt_attn, n_cnt_o, n_cnt_mlp;
+  size_t z, s_mlp, s_head, idx, heads, qkv, apart, o, h1, u, part, total;
+  int max_chunks;
 };
 
 Layout layout_of(const dv_dims* d, int B, int k, int kh) {
@@ -139,7 +139,6 @@ Layout layout_of(const dv_dims* d, int B, int k, int kh) {
   const int tpk = d->head_dim / v;
   const int kpp = 256 / tpk;
   L.max_chunks = (d->t_max + 2 * kpp - 1) / (2 * kpp);
-  L.n_slices = (d->d_model + 64 * v - 1) / (64 * v);
   L.z = take(f * Bz * (d->rank_mlp + d->rank_head));
   L.s_mlp = take(f * Bz * d->d_ffn);
   L.s_head = take(f * Bz * d->n_heads);
@@ -151,10 +150,6 @@ Layout layout_of(const dv_dims* d, int B, int k, int kh) {
   L.h1 = take(f * Bz * d->d_model);
   L.u = take(f * Bz * k);
   L.part = take(f * Bz * dv::rowaxpy_max_rg() * d->d_model);
-  L.n_cnt_attn = B * kh;
-  L.n_cnt_o = B * L.n_slices;
-  L.n_cnt_mlp = B * L.n_slices;
-  L.cnt = take(f * (L.n_cnt_attn + L.n_cnt_o + L.n_cnt_mlp));
   L.total = off;
   return L;
 }
@@ -249,26 +244,24 @@ dv_status run_topk2(const float* s_mlp, int F, int k, int32_t* idx, const float*
   return DV_OK;
 }
 
-// h_out = resid + (sum over selected heads of o_h . Wo_h + bo), x normalised with norm_g if given.
+// y = resid + (sum over selected heads of o_h . Wo_h + bo), x normalised with norm_g if given.
 dv_status run_attn(const dv_dims* d, const dv_layer* Lw, const float* x, const float* norm_g, int B,
                    const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* y,
                    const float* resid, const Layout& L, void* ws, int cus, hipStream_t st) {
   const bool f16 = is_f16(d);
   const int D = d->d_model, dh = d->head_dim, H = d->n_heads;
-  int* cnt = at<int>(ws, L.cnt);
   float* qkv = at<float>(ws, L.qkv);
   float* o = at<float>(ws, L.o);
   if (kh > 0) {
     dv::RowDotArgs a{};
     a.nseg = 1; a.d = D; a.eps = 1e-5f;
-    a.clear_ptr = cnt; a.clear_n = L.n_cnt_attn + L.n_cnt_o;
     a.seg[0] = seg_of(Lw->wqkv, D, kh * 3 * dh, 3 * dh, H, heads, kh, x, D, norm_g, Lw->bqkv, qkv,
                       (long long)kh * 3 * dh, 0);
     DV_TRY(run_rowdot(a, f16, B, cus, st, /*tag=*/1));
     dv::AttnArgs at_{};
     at_.qkv = qkv; at_.heads = heads; at_.kh = kh; at_.n_heads = H; at_.dh = dh; at_.t_past = t_past;
     at_.t_max = d->t_max; at_.k_cache = kc; at_.v_cache = vc; at_.partial = at<float>(ws, L.apart);
-    at_.counters = cnt; at_.o = o;
+    at_.o = o;
     if (!dv::attn_plan(dh, f16, t_past + 1, kh, B, cus, &at_.chunk, &at_.n_chunks))
       return fail(DV_ERR_DIMS, "head_dim unsupported");
     if (at_.n_chunks > L.max_chunks) return fail(DV_ERR_DIMS, "internal: attention chunk plan");
@@ -279,7 +272,7 @@ dv_status run_attn(const dv_dims* d, const dv_layer* Lw, const float* x, const f
   dv::rowaxpy_plan(D, kh * dh, f16, B, cus, &tpc, &r.n_slices, &r.RG);
   r.W = Lw->wo; r.ld = D; r.d = D; r.n_rows = kh * dh; r.G = dh; r.n_groups = H; r.idx = heads;
   r.idx_bstride = kh; r.coef = o; r.ldc = (long long)kh * dh; r.bias = Lw->bo; r.resid = resid; r.ldr = D;
-  r.out = y; r.ldo = D; r.partial = at<float>(ws, L.part); r.counters = cnt + L.n_cnt_attn;
+  r.out = y; r.ldo = D; r.partial = at<float>(ws, L.part);
   DV_HIP(dv::launch_rowaxpy(r, f16, tpc, B, st));
   return DV_OK;
 }
@@ -289,12 +282,10 @@ dv_status run_mlp(const dv_dims* d, const dv_layer* Lw, const float* x, const fl
                   hipStream_t st) {
   const bool f16 = is_f16(d);
   const int D = d->d_model, F = d->d_ffn;
-  int* cnt = at<int>(ws, L.cnt) + L.n_cnt_attn + L.n_cnt_o;
   float* u = at<float>(ws, L.u);
   if (k > 0) {
     dv::RowDotArgs a{};
     a.nseg = 1; a.d = D; a.eps = 1e-5f;
-    a.clear_ptr = cnt; a.clear_n = L.n_cnt_mlp;
     a.seg[0] = seg_of(Lw->w1t, D, k, 1, F, idx, k, x, D, norm_g, Lw->b1, u, k, 1);
     DV_TRY(run_rowdot(a, f16, B, cus, st));
   }
@@ -303,7 +294,7 @@ dv_status run_mlp(const dv_dims* d, const dv_layer* Lw, const float* x, const fl
   dv::rowaxpy_plan(D, k, f16, B, cus, &tpc, &r.n_slices, &r.RG);
   r.W = Lw->w2; r.ld = D; r.d = D; r.n_rows = k; r.G = 1; r.n_groups = F; r.idx = idx; r.idx_bstride = k;
   r.coef = u; r.ldc = k; r.bias = Lw->b2; r.resid = resid; r.ldr = D; r.out = y; r.ldo = D;
-  r.partial = at<float>(ws, L.part); r.counters = cnt;
+  r.partial = at<float>(ws, L.part);
   DV_HIP(dv::launch_rowaxpy(r, f16, tpc, B, st));
   return DV_OK;
 }

@@ -34,8 +34,6 @@ struct RowDotArgs {
   int nseg;
   int d;                    // row length (elements), shared by both segments
   float eps;
-  int* clear_ptr;           // block (0,0) zeroes clear_n ints (counters of later kernels)
-  int clear_n;
 };
 
 // Chooses the tiling for row length d (elements) and storage type; returns false if d is
@@ -46,8 +44,8 @@ hipError_t launch_rowdot(const RowDotArgs& a, bool f16, int B, hipStream_t s, in
 
 // ---------------------------------------------------------------------------
 // Gather row-axpy ("GEMV2"): out[b][c] = sum_i coef[b][i] * W[row_b(i)][c] + bias[c] + resid[b][c]
-//   Split over column slices (grid.x) and row groups (grid.y); row-group partials are summed
-//   in a fixed order by the last block of each slice (deterministic).
+//   Column slices x row groups write fp32 partials; a second kernel sums them in group
+//   order (no in-kernel cross-block communication).
 // ---------------------------------------------------------------------------
 struct RowAxpyArgs {
   const void* W;
@@ -65,8 +63,7 @@ struct RowAxpyArgs {
   long long ldr;
   float* out;               // [B][ldo]
   long long ldo;
-  float* partial;           // [B][RG][d]
-  int* counters;            // [B][n_slices], zero on entry; left zero on exit
+  float* partial;           // [B][RG][d] (used when RG > 1)
   int RG;
   int n_slices;
 };
@@ -76,7 +73,7 @@ int rowaxpy_max_rg();
 hipError_t launch_rowaxpy(const RowAxpyArgs& a, bool f16, int tpc, int B, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// Head-sparse decode attention with split-T partials and in-kernel combine.
+// Head-sparse decode attention: split-T partials, then a combine kernel.
 // ---------------------------------------------------------------------------
 struct AttnArgs {
   const float* qkv;         // [B][kh][3][dh] fp32 (q, k, v of each selected head)
@@ -90,8 +87,7 @@ struct AttnArgs {
   void* v_cache;
   int chunk;                // keys per block
   int n_chunks;
-  float* partial;           // [B][kh][n_chunks][dh + 2]
-  int* counters;            // [B][kh]
+  float* partial;           // [B][kh][n_chunks][dh + 2]: (m, l, o[dh]) per chunk
   float* o;                 // [B][kh][dh]
 };
 bool attn_plan(int dh, bool f16, int t_total, int kh, int B, int cus, int* chunk, int* n_chunks);

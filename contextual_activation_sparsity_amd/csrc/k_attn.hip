@@ -8,15 +8,17 @@
 //
 // Per block: scores s_t = q.K_t / sqrt(dh) with TPK = dh/VEC threads per key (a 16-byte
 // chunk each, summed by an xor butterfly), the chunk maximum m, p_t = exp(s_t - m), the
-// unnormalised p.V in fp32 and l = sum p. Partials (m, l, o) go to the workspace; the last
-// block of each head (device-scope counter) rescales and sums them in chunk order and
-// writes o_h = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M). Deterministic.
+// unnormalised p.V in fp32 and l = sum p. Partials (m, l, o) go to the workspace and a
+// second kernel rescales and sums them in chunk order:
+// o_h = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M). Deterministic; no block waits on
+// another inside a kernel.
 #include "dv_device.h"
 #include "dv_kernels.h"
 
 namespace dv {
 
 constexpr int kAttnBlock = 256;
+constexpr int kAttnStage = 40;  // chunk partials staged in LDS per sweep of the combine
 
 template <typename WT, int DH, int NPASS>
 __global__ __launch_bounds__(kAttnBlock) void attn_kernel(AttnArgs a) {
@@ -26,10 +28,10 @@ __global__ __launch_bounds__(kAttnBlock) void attn_kernel(AttnArgs a) {
   constexpr int TC = KPP * NPASS;
   constexpr int NW = kAttnBlock / kWave;
   static_assert(TPK <= kWave, "one key per wave at most");
+  static_assert(DH <= kAttnBlock, "one thread per output element in the combine");
   __shared__ float s_o[KPP][DH];
   __shared__ float s_l[KPP];
   __shared__ float s_m[NW];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int ks = tid / TPK;
@@ -147,33 +149,60 @@ __global__ __launch_bounds__(kAttnBlock) void attn_kernel(AttnArgs a) {
     part[1] = lt;
   }
 
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&a.counters[b * a.kh + s], 1);
-    s_last = (prev == a.n_chunks - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
+// Combine the chunk partials of one (batch row, selected head): M = max m_c,
+// o = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M), in chunk order (deterministic). The
+// partials are staged in LDS with coalesced sweeps.
+template <int DH>
+__global__ __launch_bounds__(kAttnBlock) void attn_combine_kernel(AttnArgs a) {
+  __shared__ float s_part[kAttnStage * (DH + 2)];
+  const int tid = threadIdx.x;
+  const int s = blockIdx.x;
+  const int b = blockIdx.y;
   const float* base = a.partial + ((long long)b * a.kh + s) * a.n_chunks * (DH + 2);
-  float M = -INFINITY;
-  for (int cc = 0; cc < a.n_chunks; ++cc) M = fmaxf(M, base[cc * (DH + 2)]);
   float* o = a.o + ((long long)b * a.kh + s) * DH;
-  for (int e = tid; e < DH; e += kAttnBlock) {
-    float L = 0.f, O = 0.f;
-    if (M > -INFINITY) {
-      for (int cc = 0; cc < a.n_chunks; ++cc) {
-        const float mc = base[cc * (DH + 2)];
+  const int e = tid;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  const bool one_sweep = a.n_chunks <= kAttnStage;
+  // all loads of a sweep are issued before any is stored
+  constexpr int QMAX = (kAttnStage * (DH + 2) + kAttnBlock - 1) / kAttnBlock;
+  auto stage = [&](int c0, int nb) {
+    const int n = nb * (DH + 2);
+    const float* src = base + (long long)c0 * (DH + 2);
+    float v[QMAX];
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+      const int i = tid + q * kAttnBlock;
+      v[q] = i < n ? src[i] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+      const int i = tid + q * kAttnBlock;
+      if (i < n) s_part[i] = v[q];
+    }
+    __syncthreads();
+  };
+  for (int c0 = 0; c0 < a.n_chunks; c0 += kAttnStage) {
+    const int nb = min(kAttnStage, a.n_chunks - c0);
+    stage(c0, nb);
+    for (int cc = 0; cc < nb; ++cc) M = fmaxf(M, s_part[cc * (DH + 2)]);
+    if (one_sweep) break;
+  }
+  for (int c0 = 0; c0 < a.n_chunks; c0 += kAttnStage) {
+    const int nb = min(kAttnStage, a.n_chunks - c0);
+    if (!one_sweep) stage(c0, nb);
+    if (e < DH && M > -INFINITY) {
+      for (int cc = 0; cc < nb; ++cc) {
+        const float mc = s_part[cc * (DH + 2)];
         const float f = (mc > -INFINITY) ? exp2f(mc - M) : 0.f;
-        L = fmaf(base[cc * (DH + 2) + 1], f, L);
-        O = fmaf(base[cc * (DH + 2) + 2 + e], f, O);
+        L = fmaf(s_part[cc * (DH + 2) + 1], f, L);
+        O = fmaf(s_part[cc * (DH + 2) + 2 + e], f, O);
       }
     }
-    o[e] = (L > 0.f) ? O / L : 0.f;
   }
-  if (tid == 0) a.counters[b * a.kh + s] = 0;
+  if (e < DH) o[e] = (L > 0.f) ? O / L : 0.f;
 }
 
 bool attn_plan(int dh, bool f16, int t_total, int kh, int B, int cus, int* chunk, int* n_chunks) {
@@ -203,6 +232,9 @@ static hipError_t launch_dh(const AttnArgs& a, int B, hipStream_t s) {
     case 8: hipLaunchKernelGGL((attn_kernel<WT, DH, 8>), grid, dim3(kAttnBlock), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_combine_kernel<DH>), dim3(a.kh, B), dim3(kAttnBlock), 0, s, a);
   return hipGetLastError();
 }
 

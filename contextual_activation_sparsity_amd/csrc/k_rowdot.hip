@@ -17,9 +17,19 @@
 namespace dv {
 
 constexpr int kRowdotBlock = 256;
+// Tile parameters (compile-time; the defaults are the tuned values).
+#ifndef DV_ROWDOT_BPC_BIG
+#define DV_ROWDOT_BPC_BIG 2  // target resident blocks per CU for long rows (>= 5 chunks/thread)
+#endif
+#ifndef DV_ROWDOT_BPC
+#define DV_ROWDOT_BPC 4      // target resident blocks per CU otherwise
+#endif
+#ifndef DV_ROWDOT_RBIG
+#define DV_ROWDOT_RBIG 4     // rows in flight per row-slot when a thread holds >= 5 chunks
+#endif
 
 __host__ __device__ constexpr int rowdot_rows_in_flight(int ch) {
-  return ch >= 5 ? 2 : (ch >= 3 ? 4 : (ch == 2 ? 6 : 8));
+  return ch >= 5 ? DV_ROWDOT_RBIG : (ch >= 3 ? 4 : (ch == 2 ? 6 : 8));
 }
 
 // TAG only separates launch sites in profiles (1 = head-sparse q/k/v projection).
@@ -40,15 +50,16 @@ __global__ __launch_bounds__(kRowdotBlock) void rowdot_kernel(RowDotArgs a) {
   if (second) bx -= a.seg[0].blocks;
   const RowDotSeg S = second ? a.seg[1] : a.seg[0];
 
-  if (a.clear_ptr != nullptr && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = tid; i < a.clear_n; i += kRowdotBlock) a.clear_ptr[i] = 0;
-
   const int slot = tid / TPR;
   const int lr = tid % TPR;
   const int wr = lr / kWave;  // wave index within the row (0 when TPR <= 64)
   const int nchunk = a.d / VEC;
+  const WT* W = reinterpret_cast<const WT*>(S.W);
+  const int TS = S.blocks * SLOTS;  // row-slots of this segment
+  const int32_t* idxb = S.idx ? S.idx + (long long)b * S.idx_bstride : nullptr;
+  float* outb = S.out + (long long)b * S.ldo;
 
-  // Input slice of this thread, widened to fp32, in registers.
+  // Input slice of this thread, widened to fp32, in registers (requested first).
   float xr[CH][VEC];
   const float* xb = S.x + (long long)b * S.ldx;
 #pragma unroll
@@ -67,45 +78,12 @@ __global__ __launch_bounds__(kRowdotBlock) void rowdot_kernel(RowDotArgs a) {
     }
   }
 
-  if (S.norm_g != nullptr) {
-    // RMSNorm folded into the prologue: the threads of a row-slot hold the whole vector.
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) ss = fmaf(xr[j][e], xr[j][e], ss);
-    ss = group_sum<GW>(ss);
-    if constexpr (WPR > 1) {
-      if ((lr % kWave) == 0) s_norm[slot][wr] = ss;
-      __syncthreads();
-      ss = 0.f;
-#pragma unroll
-      for (int w = 0; w < WPR; ++w) ss += s_norm[slot][w];
-    }
-    const float inv = 1.0f / sqrtf(ss / (float)a.d + a.eps);
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int c = lr + TPR * j;
-      if (c < nchunk) {
-#pragma unroll
-        for (int v = 0; v < VEC / 4; ++v) {
-          const f32x4 g = *reinterpret_cast<const f32x4*>(S.norm_g + c * VEC + 4 * v);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) xr[j][4 * v + e] = xr[j][4 * v + e] * inv * g[e];
-        }
-      }
-    }
-  }
-
-  const WT* W = reinterpret_cast<const WT*>(S.W);
-  const int TS = S.blocks * SLOTS;  // row-slots of this segment
-  const int32_t* idxb = S.idx ? S.idx + (long long)b * S.idx_bstride : nullptr;
-  float* outb = S.out + (long long)b * S.ldo;
-
-  // Block-uniform loop so the barriers below are reached by every thread.
-  for (int base = bx * SLOTS; base < S.n_out; base += TS * R) {
-    long long row[R];
-    bool rv[R];
+  // Rows of the batch starting at `base` and their weight loads. The first batch is
+  // requested before the input norm is computed so the two latencies overlap.
+  long long row[R];
+  bool rv[R];
+  Chunk<WT> w[R][CH];
+  auto issue = [&](int base) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int i = base + slot + r * TS;
@@ -124,7 +102,6 @@ __global__ __launch_bounds__(kRowdotBlock) void rowdot_kernel(RowDotArgs a) {
         }
       }
     }
-    Chunk<WT> w[R][CH];
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -133,6 +110,42 @@ __global__ __launch_bounds__(kRowdotBlock) void rowdot_kernel(RowDotArgs a) {
         if (rv[r] && c < nchunk) w[r][j] = load_chunk<WT>(W + row[r] * S.ld + (long long)c * VEC);
         else w[r][j].raw = u32x4{0u, 0u, 0u, 0u};
       }
+  };
+  int base = bx * SLOTS;
+  if (base < S.n_out) issue(base);
+
+  if (S.norm_g != nullptr) {
+    // RMSNorm folded into the prologue: the threads of a row-slot hold the whole vector.
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ss = fmaf(xr[j][e], xr[j][e], ss);
+    ss = group_sum<GW>(ss);
+    if constexpr (WPR > 1) {
+      if ((lr % kWave) == 0) s_norm[slot][wr] = ss;
+      __syncthreads();
+      ss = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < WPR; ++w2) ss += s_norm[slot][w2];
+    }
+    const float inv = 1.0f / sqrtf(ss / (float)a.d + a.eps);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = lr + TPR * j;
+      if (c < nchunk) {
+#pragma unroll
+        for (int v = 0; v < VEC / 4; ++v) {
+          const f32x4 g = *reinterpret_cast<const f32x4*>(S.norm_g + c * VEC + 4 * v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xr[j][4 * v + e] = xr[j][4 * v + e] * inv * g[e];
+        }
+      }
+    }
+  }
+
+  // Block-uniform loop so the barriers below are reached by every thread.
+  for (; base < S.n_out; base += TS * R) {
     float acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -146,6 +159,12 @@ __global__ __launch_bounds__(kRowdotBlock) void rowdot_kernel(RowDotArgs a) {
       }
       acc[r] = group_sum<GW>(acc[r]);
     }
+    long long row_done[R];
+    bool rv_done[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) { row_done[r] = row[r]; rv_done[r] = rv[r]; }
+    // next batch's loads go out before this batch's reduction and store
+    if (base + TS * R < S.n_out) issue(base + TS * R);
     if constexpr (WPR > 1) {
       if ((lr % kWave) == 0)
 #pragma unroll
@@ -167,8 +186,8 @@ __global__ __launch_bounds__(kRowdotBlock) void rowdot_kernel(RowDotArgs a) {
         const int i = base + slot + r * TS;
         if (i < S.n_out) {
           float v = 0.f;
-          if (rv[r]) {
-            v = acc[r] + (S.bias ? S.bias[row[r]] : 0.f);
+          if (rv_done[r]) {
+            v = acc[r] + (S.bias ? S.bias[row_done[r]] : 0.f);
             if (S.relu) v = fmaxf(v, 0.f);
           }
           outb[i] = v;
@@ -202,10 +221,9 @@ bool rowdot_plan(int d, bool f16, int* tpr, int* ch) {
 }
 
 int rowdot_blocks_for(int n_out, int tpr, int ch, int cus) {
-  (void)ch;
   if (n_out <= 0) return 1;
   const int slots = kRowdotBlock / tpr;
-  const long long target = (long long)cus * 4;
+  const long long target = (long long)cus * (ch >= 5 ? DV_ROWDOT_BPC_BIG : DV_ROWDOT_BPC);
   const long long per_slot = ((long long)n_out + target * slots - 1) / (target * slots);
   long long blocks = ((long long)n_out + per_slot * slots - 1) / (per_slot * slots);
   if (blocks < 1) blocks = 1;

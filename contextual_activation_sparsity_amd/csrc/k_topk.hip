@@ -4,8 +4,8 @@
 //
 // One block per (row, problem). Each thread owns a contiguous run of indices and keeps
 // their 32-bit order keys in registers: finite floats map monotonically to unsigned
-// keys with -0.0 folded onto +0.0, and every NaN maps to 0, below -inf. Four passes over
-// 8-bit digits (histograms privatised per wavefront in LDS, then summed) find the k-th
+// keys with -0.0 folded onto +0.0, and every NaN maps to 0, below -inf. Three passes over
+// 11/11/10-bit digits (LDS histograms in four copies to spread atomics) find the k-th
 // largest key tau and how many keys equal to tau are still needed. The output is written
 // in ascending index order from a block-wide exclusive scan of per-thread counts: every
 // key above tau, plus the lowest-index keys equal to tau. Integer-exact and unique.
@@ -21,6 +21,7 @@ __device__ __forceinline__ unsigned order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Exclusive scan over the block of up to two per-thread counts (thread order).
 template <int BS>
 __device__ __forceinline__ void block_excl_scan2(unsigned a, unsigned b, unsigned* ea, unsigned* eb,
                                                  unsigned (*s)[BS / kWave]) {
@@ -39,13 +40,17 @@ __device__ __forceinline__ void block_excl_scan2(unsigned a, unsigned b, unsigne
   for (int i = 0; i < w; ++i) { pa += s[0][i]; pb += s[1][i]; }
   *ea = pa + ia - a;
   *eb = pb + ib - b;
+  __syncthreads();
 }
+
+constexpr int kTopkBins = 2048;   // 11-bit digits: passes over bits 31..21, 20..10, 9..0
+constexpr int kTopkCopies = 4;    // histogram copies (wave w uses copy w % 4) to spread LDS atomics
 
 template <int BS, int KPT>
 __global__ __launch_bounds__(BS) void topk_kernel(TopkArgs a) {
   constexpr int NW = BS / kWave;
-  __shared__ unsigned s_hist[NW][256];
-  __shared__ unsigned s_tot[256];
+  constexpr int BPT = kTopkBins / BS;  // bins per thread in the digit search
+  __shared__ unsigned s_hist[kTopkCopies][kTopkBins];
   __shared__ unsigned s_sel[2];
   __shared__ unsigned s_scan[2][NW];
 
@@ -54,7 +59,7 @@ __global__ __launch_bounds__(BS) void topk_kernel(TopkArgs a) {
   const int n = P.n;
   const int k = P.k;
   const int tid = threadIdx.x;
-  const int w = tid / kWave;
+  const int copy = (tid / kWave) % kTopkCopies;
   if (k <= 0) return;
   int32_t* out = P.out + (long long)b * k;
   if (k >= n) {
@@ -67,51 +72,60 @@ __global__ __launch_bounds__(BS) void topk_kernel(TopkArgs a) {
   const int nv = max(0, min(per, n - beg));
 
   unsigned key[KPT];
+  if ((per % 4) == 0 && (n % 4) == 0 && (reinterpret_cast<uintptr_t>(sc) & 15u) == 0) {
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) key[j] = (j < nv) ? order_key(sc[beg + j]) : 0u;
+    for (int j = 0; j < KPT; j += 4) {
+      if (j < nv) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(sc + beg + j);
+        key[j] = order_key(v[0]); key[j + 1] = order_key(v[1]);
+        key[j + 2] = order_key(v[2]); key[j + 3] = order_key(v[3]);
+      } else {
+        key[j] = key[j + 1] = key[j + 2] = key[j + 3] = 0u;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = (j < nv) ? order_key(sc[beg + j]) : 0u;
+  }
 
+  if (tid == 0) { s_sel[0] = 0u; s_sel[1] = 1u; }
   unsigned prefix = 0u, pmask = 0u, krem = (unsigned)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < NW * 256; i += BS) (&s_hist[0][0])[i] = 0u;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const unsigned dmask = pass == 2 ? 1023u : 2047u;
+    for (int i = tid; i < kTopkCopies * kTopkBins; i += BS) (&s_hist[0][0])[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if (j < nv && (key[j] & pmask) == prefix) atomicAdd(&s_hist[w][(key[j] >> shift) & 255u], 1u);
+      if (j < nv && (key[j] & pmask) == prefix) atomicAdd(&s_hist[copy][(key[j] >> shift) & dmask], 1u);
     __syncthreads();
-    for (int i = tid; i < 256; i += BS) {
-      unsigned t = 0;
+    // thread t owns BPT consecutive bins in descending digit order
+    unsigned cnt[BPT], tot = 0;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) t += s_hist[ww][i];
-      s_tot[i] = t;
+    for (int j = 0; j < BPT; ++j) {
+      const int bin = kTopkBins - 1 - (tid * BPT + j);
+      unsigned c = 0;
+#pragma unroll
+      for (int q = 0; q < kTopkCopies; ++q) c += s_hist[q][bin];
+      cnt[j] = c;
+      tot += c;
     }
-    __syncthreads();
-    if (tid < kWave) {
-      // lane l owns bins 255-4l .. 252-4l (descending digit order)
-      unsigned cnt[4], tot = 0;
+    unsigned before, unused;
+    block_excl_scan2<BS>(tot, 0u, &before, &unused, s_scan);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { cnt[j] = s_tot[255 - 4 * tid - j]; tot += cnt[j]; }
-      unsigned incl = tot;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const unsigned t = __shfl_up(incl, off, kWave);
-        if (tid >= off) incl += t;
+    for (int j = 0; j < BPT; ++j) {
+      if (before < krem && krem <= before + cnt[j]) {
+        s_sel[0] = (unsigned)(kTopkBins - 1 - (tid * BPT + j));
+        s_sel[1] = krem - before;
       }
-      unsigned before = incl - tot;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (before < krem && krem <= before + cnt[j]) {
-          s_sel[0] = 255u - 4u * tid - j;
-          s_sel[1] = krem - before;
-        }
-        before += cnt[j];
-      }
+      before += cnt[j];
     }
     __syncthreads();
     const unsigned dgt = s_sel[0];
     krem = s_sel[1];
     prefix |= dgt << shift;
-    pmask |= 255u << shift;
+    pmask |= dmask << shift;
     __syncthreads();
   }
   const unsigned tau = prefix;
@@ -128,10 +142,15 @@ __global__ __launch_bounds__(BS) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     if (j < nv) {
+      // pos < k always holds for a correct selection; the bound keeps writes in range regardless
       if (key[j] > tau) {
-        out[pos++] = beg + j;
+        if (pos < (unsigned)k) out[pos] = beg + j;
+        ++pos;
       } else if (key[j] == tau) {
-        if (eq_seen < krem) out[pos++] = beg + j;
+        if (eq_seen < krem) {
+          if (pos < (unsigned)k) out[pos] = beg + j;
+          ++pos;
+        }
         ++eq_seen;
       }
     }

@@ -3,7 +3,7 @@
 // Element i of a stream with key K is the SplitMix64 output mix64(K + (i+1)*0x9E3779B97F4A7C15)
 // (Steele, Lea and Flood, OOPSLA 2014). Its four 16-bit lanes are summed, the sum is centred
 // by the exact integer 2*65535, converted exactly to fp32 and multiplied once by an fp32
-// scale; fp16 storage rounds that product to nearest-even. The host implementation does the
+// scale; fp16 storage rounds that product to nearest-even (explicitly, below). The host implementation does the
 // same operations, so both produce identical bits. This file draws numbers only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -23,11 +23,41 @@ __device__ __forceinline__ float draw(uint64_t key, uint64_t ctr, float scale) {
   return __fmul_rn(z, scale);
 }
 
-template <typename T>
-__global__ void fill_kernel(T* out, long long n, uint64_t key, float scale, long long start) {
+// IEEE 754 binary32 -> binary16, round to nearest, ties to even, written out in integer
+// arithmetic so the result does not depend on which conversion instruction the compiler
+// picks (the packed conversion rounded an exact tie differently from the host).
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  const uint32_t x = __float_as_uint(f);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7fffffffu;
+  if (ax >= 0x7f800000u) return (uint16_t)(sign | 0x7c00u | (ax > 0x7f800000u ? 0x200u : 0u));  // inf, nan
+  if (ax >= 0x47800000u) return (uint16_t)(sign | 0x7c00u);   // overflow to inf (|f| >= 65536)
+  if (ax < 0x38800000u) {                                     // below the smallest normal half
+    if (ax < 0x33000000u) return (uint16_t)sign;              // below half the smallest subnormal
+    const uint32_t m = (ax & 0x7fffffu) | 0x800000u;
+    const int sh = 126 - (int)(ax >> 23);                     // 14..24
+    uint32_t q = m >> sh;
+    const uint32_t rem = m & ((1u << sh) - 1u), half = 1u << (sh - 1);
+    q += (rem > half) || (rem == half && (q & 1u));
+    return (uint16_t)(sign | q);
+  }
+  const uint32_t t = ax - 0x38000000u;                        // rebias the exponent 127 -> 15
+  uint32_t q = t >> 13;
+  const uint32_t rem = t & 0x1fffu;
+  q += (rem > 0x1000u) || (rem == 0x1000u && (q & 1u));       // a carry may bump the exponent
+  return (uint16_t)(sign | q);
+}
+
+__global__ void fill_f32_kernel(float* out, long long n, uint64_t key, float scale, long long start) {
   const long long stride = (long long)gridDim.x * blockDim.x;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    out[i] = (T)draw(key, (uint64_t)(start + i), scale);
+    out[i] = draw(key, (uint64_t)(start + i), scale);
+}
+
+__global__ void fill_f16_kernel(uint16_t* out, long long n, uint64_t key, float scale, long long start) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    out[i] = f32_to_f16_rne(draw(key, (uint64_t)(start + i), scale));
 }
 
 }  // namespace
@@ -43,11 +73,11 @@ int dv_synth_fill(void* out, long long n, int dtype, unsigned long long key, flo
   long long blocks = (n + threads - 1) / threads;
   if (blocks > 65536) blocks = 65536;
   if (dtype == 0)
-    hipLaunchKernelGGL(fill_kernel<float>, dim3((unsigned)blocks), dim3(threads), 0, stream,
+    hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                        static_cast<float*>(out), n, (uint64_t)key, scale, start);
   else
-    hipLaunchKernelGGL(fill_kernel<_Float16>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       static_cast<_Float16*>(out), n, (uint64_t)key, scale, start);
+    hipLaunchKernelGGL(fill_f16_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                       static_cast<uint16_t*>(out), n, (uint64_t)key, scale, start);
   return (int)hipGetLastError();
 }
 

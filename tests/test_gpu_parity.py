@@ -176,7 +176,13 @@ def test_sparse_attn(dv, host_layers, w, case):
         for h in range(H):
             if h in set(Sh[b].tolist()):
                 for m, (got_c, name) in enumerate(((kg, "k"), (vg, "v")), start=1):
-                    assert_close(got_c[b, h, T], ref["qkv"][b, h, m], w.dtype, f"appended {name}")
+                    # the slot holds the fp32 projection rounded to the storage type
+                    r = ref["qkv"][b, h, m]
+                    ulp = 2.0 ** -10 if w.dtype == "f16" else 2.0 ** -23
+                    err = np.abs(got_c[b, h, T].astype(np.float64) - r)
+                    assert np.all(err <= ulp * np.abs(r) + 1e-4 * rms(r)), f"appended {name}"
+                    assert np.max(err) <= 2e-2 * rms(r), f"appended {name}: north-star bar"
+
                     kg_ = got_c[b, h].copy()
                     kg_[T] = (kc if name == "k" else vc)[b, h, T]
                     assert np.array_equal(kg_, (kc if name == "k" else vc)[b, h])
