@@ -39,6 +39,9 @@ def main() -> int:
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serial", action="store_true", help="run the predictor on the main stream")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
@@ -85,30 +88,64 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.float16, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)   # 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] calibration copy of 1 GiB done")
 
-    # Timed region: K steps; the q/k/v gather launches carry HIP event pairs on their stream.
+    def timed(run_step, n):
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        h0 = time.perf_counter()
+        for i in range(n):
+            run_step(args.warmup + i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n, (time.perf_counter() - h0) * 1e3 / n
+
+    # (1) eager launches, no instrumentation
+    ms_eager, wall_eager = timed(step, args.steps)
+    log(f"[bench] eager: {ms_eager:.3f} ms/step ({ms_eager * 1e3 / L:.2f} us/layer-token, host {wall_eager:.3f} ms)")
+
+    # (2) the whole two-stream step captured once in a HIP graph and replayed (fresh x is
+    #     copied into the graph's input buffer before each replay)
+    ms_graph = None
+    if not args.no_graph:
+        x_in = torch.empty(1, w.d_model, device="cuda")
+        x_in.copy_(xs[0])
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            dv.dv_lookahead_stack(dims, layers, preds, x_in, w.k, w.kh, kcs, vcs, w.t_past, y, ws=ws,
+                                  side_stream=side)
+        torch.cuda.synchronize()
+
+        def gstep(i):
+            x_in.copy_(xs[i])
+            graph.replay()
+        for i in range(3):
+            gstep(i)
+        ms_graph, wall_graph = timed(gstep, args.steps)
+        log(f"[bench] graph: {ms_graph:.3f} ms/step ({ms_graph * 1e3 / L:.2f} us/layer-token, host {wall_graph:.3f} ms)")
+
+    # (3) eager again with HIP event pairs around every q/k/v gather launch (on its stream)
     n_ev = args.steps * L
     assert _lib.lib().dv_timing_start(n_ev) == n_ev
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record()
-    h0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - h0
-    ms_total = ev0.elapsed_time(ev1)
+    ms_hooked, _ = timed(step, args.steps)
     import ctypes
     qkv_ms = (ctypes.c_float * n_ev)()
     got = _lib.lib().dv_timing_stop(qkv_ms, n_ev)
     assert got == n_ev, f"timing hook recorded {got} of {n_ev}"
     qkv_ms = np.array(qkv_ms[:n_ev], dtype=np.float64)
-    ms_per_step = ms_total / args.steps
+    log(f"[bench] instrumented eager pass: {ms_hooked:.3f} ms/step")
+
+    ms_per_step = ms_graph if ms_graph is not None else ms_eager
     us_per_layer = ms_per_step * 1e3 / L
-    log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step, {us_per_layer:.2f} us/layer-token "
-        f"(host wall {wall * 1e3 / args.steps:.3f} ms/step)")
 
     tb = traffic.step_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.t_past, w.k, w.kh, 2)
     step_bytes = tb["total"]
@@ -136,7 +173,10 @@ def main() -> int:
                    "layers": L, "d_model": w.d_model, "d_ffn": w.d_ffn, "n_heads": w.n_heads,
                    "head_dim": w.head_dim, "kv_len": w.t_past, "rank": w.rank, "k": w.k, "kh": w.kh,
                    "batch": 1, "storage": "f16 weights and KV, fp32 activations and accumulation",
-                   "side_stream": not args.serial},
+                   "side_stream": not args.serial,
+                   "launch": "hip graph replay" if ms_graph is not None else "eager"},
+        "ms_per_step_eager": round(ms_eager, 4),
+        "ms_per_step_graph": round(ms_graph, 4) if ms_graph is not None else None,
         "achieved_GBps": round(gbps, 1),
         "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "bytes_per_layer_token": int(step_bytes),

@@ -247,17 +247,20 @@ dv_status run_topk2(const float* s_mlp, int F, int k, int32_t* idx, const float*
 // y = resid + (sum over selected heads of o_h . Wo_h + bo), x normalised with norm_g if given.
 dv_status run_attn(const dv_dims* d, const dv_layer* Lw, const float* x, const float* norm_g, int B,
                    const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* y,
-                   const float* resid, const Layout& L, void* ws, int cus, hipStream_t st) {
+                   const float* resid, const Layout& L, void* ws, int cus, hipStream_t st,
+                   hipEvent_t ev_after_qkv = nullptr) {
   const bool f16 = is_f16(d);
   const int D = d->d_model, dh = d->head_dim, H = d->n_heads;
   float* qkv = at<float>(ws, L.qkv);
   float* o = at<float>(ws, L.o);
+  if (kh == 0 && ev_after_qkv) DV_HIP(hipEventRecord(ev_after_qkv, st));
   if (kh > 0) {
     dv::RowDotArgs a{};
     a.nseg = 1; a.d = D; a.eps = 1e-5f;
     a.seg[0] = seg_of(Lw->wqkv, D, kh * 3 * dh, 3 * dh, H, heads, kh, x, D, norm_g, Lw->bqkv, qkv,
                       (long long)kh * 3 * dh, 0);
     DV_TRY(run_rowdot(a, f16, B, cus, st, /*tag=*/1));
+    if (ev_after_qkv) DV_HIP(hipEventRecord(ev_after_qkv, st));
     dv::AttnArgs at_{};
     at_.qkv = qkv; at_.heads = heads; at_.kh = kh; at_.n_heads = H; at_.dh = dh; at_.t_past = t_past;
     at_.t_max = d->t_max; at_.k_cache = kc; at_.v_cache = vc; at_.partial = at<float>(ws, L.apart);
@@ -301,9 +304,9 @@ dv_status run_mlp(const dv_dims* d, const dv_layer* Lw, const float* x, const fl
 
 dv_status run_layer(const dv_dims* d, const dv_layer* Lw, const float* x, int B, const int32_t* idx, int k,
                     const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* x_out,
-                    const Layout& L, void* ws, int cus, hipStream_t st) {
+                    const Layout& L, void* ws, int cus, hipStream_t st, hipEvent_t ev_after_qkv = nullptr) {
   float* h1 = at<float>(ws, L.h1);
-  DV_TRY(run_attn(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, t_past, h1, x, L, ws, cus, st));
+  DV_TRY(run_attn(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, t_past, h1, x, L, ws, cus, st, ev_after_qkv));
   DV_TRY(run_mlp(d, Lw, h1, Lw->g2, B, idx, k, x_out, h1, L, ws, cus, st));
   return DV_OK;
 }
@@ -576,7 +579,7 @@ dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const 
   DV_TRY(predict_sets(0, h_in(0), ws, stream));
   for (int l = 0; l < n_layers; ++l) {
     if (l + 1 < n_layers) {
-      // Sets of layer l+1 from the input of layer l, overlapping layer l.
+      // Sets of layer l+1 from the input of layer l, on the side stream while layer l runs.
       if (two) {
         DV_HIP(hipEventRecord(di->ev_in, stream));
         DV_HIP(hipStreamWaitEvent(side_stream, di->ev_in, 0));

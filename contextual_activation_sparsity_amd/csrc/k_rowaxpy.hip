@@ -135,10 +135,12 @@ __global__ __launch_bounds__(kAxpyBlock) void rowaxpy_part_kernel(RowAxpyArgs a)
   }
 }
 
-// out[b][c] = sum_rg partial[b][rg][c] (group order) + bias[c] + resid[b][c]; 4 columns per thread.
-__global__ __launch_bounds__(256) void rowaxpy_reduce_kernel(RowAxpyArgs a) {
+// out[b][c] = sum_rg partial[b][rg][c] (group order) + bias[c] + resid[b][c]; 4 columns per
+// thread, small blocks so the few hundred KB of partials are read by many CUs at once.
+constexpr int kReduceBlock = 64;
+__global__ __launch_bounds__(kReduceBlock) void rowaxpy_reduce_kernel(RowAxpyArgs a) {
   const int b = blockIdx.y;
-  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int c0 = (blockIdx.x * kReduceBlock + threadIdx.x) * 4;
   if (c0 >= a.d) return;
   const float* p = a.partial + (long long)b * a.RG * a.d + c0;
   f32x4 v[kAxpyMaxRG];
@@ -179,7 +181,8 @@ hipError_t launch_rowaxpy(const RowAxpyArgs& a, bool f16, int tpc, int B, hipStr
   else hipLaunchKernelGGL((rowaxpy_part_kernel<float, kAxpyTpc>), grid, dim3(kAxpyBlock), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.RG == 1) return e;
-  hipLaunchKernelGGL(rowaxpy_reduce_kernel, dim3((a.d / 4 + 255) / 256, B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(rowaxpy_reduce_kernel, dim3((a.d / 4 + kReduceBlock - 1) / kReduceBlock, B),
+                     dim3(kReduceBlock), 0, s, a);
   return hipGetLastError();
 }
 
