@@ -200,9 +200,7 @@ dv_status run_rowdot(dv::RowDotArgs& a, bool f16, int B, int cus, hipStream_t st
       ++g_timing.cursor;
     }
   }
-  if (e0) DV_HIP(hipEventRecord(e0, st));
-  DV_HIP(dv::launch_rowdot(a, f16, B, st, tag));
-  if (e1) DV_HIP(hipEventRecord(e1, st));
+  DV_HIP(dv::launch_rowdot(a, f16, B, st, tag, e0, e1));
   return DV_OK;
 }
 

@@ -40,7 +40,8 @@ struct RowDotArgs {
 // not supported. rows_in_flight: rows one block keeps loading at once.
 bool rowdot_plan(int d, bool f16, int* tpr, int* ch);
 int rowdot_blocks_for(int n_out, int tpr, int ch, int cus);
-hipError_t launch_rowdot(const RowDotArgs& a, bool f16, int B, hipStream_t s, int tag);
+hipError_t launch_rowdot(const RowDotArgs& a, bool f16, int B, hipStream_t s, int tag,
+                         hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 
 // ---------------------------------------------------------------------------
 // Gather row-axpy ("GEMV2"): out[b][c] = sum_i coef[b][i] * W[row_b(i)][c] + bias[c] + resid[b][c]

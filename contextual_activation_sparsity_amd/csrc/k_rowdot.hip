@@ -11,6 +11,8 @@
 // keeps R rows per row-slot in flight (R*CH 16-byte loads per thread) to cover HBM latency.
 // Rows are dealt to row-slots round-robin across the grid. The dot product is summed in
 // a fixed order (per-thread chunks, xor butterfly, waves in order): bitwise deterministic.
+#include <hip/hip_ext.h>
+
 #include "dv_device.h"
 #include "dv_kernels.h"
 
@@ -257,7 +259,8 @@ static RowdotFn pick(int tpr, int ch) {
   return nullptr;
 }
 
-hipError_t launch_rowdot(const RowDotArgs& a, bool f16, int B, hipStream_t s, int tag) {
+hipError_t launch_rowdot(const RowDotArgs& a, bool f16, int B, hipStream_t s, int tag, hipEvent_t ev_begin,
+                         hipEvent_t ev_end) {
   int tpr = 0, ch = 0;
   if (!rowdot_plan(a.d, f16, &tpr, &ch)) return hipErrorInvalidValue;
   RowdotFn fn = tag == 1 ? (f16 ? pick<half_t, 1>(tpr, ch) : pick<float, 1>(tpr, ch))
@@ -265,7 +268,12 @@ hipError_t launch_rowdot(const RowDotArgs& a, bool f16, int B, hipStream_t s, in
   if (fn == nullptr) return hipErrorInvalidValue;
   int blocks = 0;
   for (int i = 0; i < a.nseg; ++i) blocks += a.seg[i].blocks;
-  hipLaunchKernelGGL(fn, dim3(blocks, B), dim3(kRowdotBlock), 0, s, a);
+  if (ev_begin != nullptr || ev_end != nullptr) {
+    // The events take this dispatch's own begin/end timestamps (not markers around it).
+    hipExtLaunchKernelGGL(fn, dim3(blocks, B), dim3(kRowdotBlock), 0, s, ev_begin, ev_end, 0u, a);
+  } else {
+    hipLaunchKernelGGL(fn, dim3(blocks, B), dim3(kRowdotBlock), 0, s, a);
+  }
   return hipGetLastError();
 }
 
