@@ -27,6 +27,18 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "rowdot_qkv_opt175b_stack24_hbm_traffic.txt")
 
 
+def source_text(spec: str) -> bytes:
+    """Bytes of a source file, or of the part of it between two marker lines when the spec
+    reads "path#first marker#next marker" (the marker of the following section ends it)."""
+    path, *marks = spec.split("#")
+    data = open(os.path.join(HERE, path), "rb").read()
+    if marks:
+        start = data.index(marks[0].encode())
+        end = data.index(marks[1].encode(), start)
+        data = data[start:end]
+    return data
+
+
 def measured_traffic(log):
     """HBM bytes per q/k/v gather launch from the committed FETCH_SIZE/WRITE_SIZE counter
     summary (scaled by a plain copy's counter reading), or None when that summary is missing
@@ -37,7 +49,7 @@ def measured_traffic(log):
         rec = json.loads(line[len("traffic_json "):])
         h = hashlib.sha256()
         for src in rec["sources"]:
-            h.update(open(os.path.join(HERE, src), "rb").read())
+            h.update(source_text(src))
     except (OSError, StopIteration, ValueError, KeyError) as e:
         log(f"[bench] no usable traffic summary ({e!r}); traffic = null")
         return None
@@ -172,11 +184,16 @@ def main() -> int:
     tb = traffic.step_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.t_past, w.k, w.kh, 2)
     step_bytes = tb["total"]
     gbps = step_bytes / (us_per_layer * 1e-6) / 1e9
-    # q/k/v gather launch: weight rows + biases of the selected heads, input x, gains, q/k/v out
-    d, dh, kh = w.d_model, w.head_dim, w.kh
+    # q/k/v gather launch: weight rows + biases of the selected heads, input x, gains, q/k/v
+    # out; in layers 0..L-2 the next layer's predictor stage 1 (both rank-r factors over the
+    # same x, z out) rides in the same launch.
+    d, dh, kh, r = w.d_model, w.head_dim, w.kh, w.rank
     qkv_bytes = 3 * kh * dh * d * 2 + 3 * kh * dh * 4 + d * 4 + d * 4 + 3 * kh * dh * 4 + kh * 4
+    p1_bytes = 2 * r * d * 2 + 2 * r * 4
+    launch_bytes = np.array([qkv_bytes + (p1_bytes if l + 1 < L else 0) for l in range(L)] * args.steps,
+                            dtype=np.float64)
     qkv_avg_us = float(np.mean(qkv_ms)) * 1e3
-    qkv_gbps = qkv_bytes / (qkv_avg_us * 1e-6) / 1e9
+    qkv_gbps = float(launch_bytes.sum()) / (float(qkv_ms.sum()) * 1e-3) / 1e9
 
     out = {
         "metric": "µs per sparse decode layer-token + achieved HBM GB/s (% of peak), OPT-175B shape",
@@ -205,8 +222,9 @@ def main() -> int:
         "bytes_breakdown": {k: int(v) for k, v in tb.items()},
         "roofline": {"bound": "hbm", "achieved": round(qkv_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(qkv_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(log),
-                     "kernel": "rowdot_kernel<f16,256,6,qkv> (head-sparse q/k/v gather-GEMV)",
-                     "bytes_per_launch": int(qkv_bytes), "avg_launch_us": round(qkv_avg_us, 3),
+                     "kernel": "rowdot_kernel<f16,256,6,qkv>: head-sparse q/k/v gather-GEMV + next layer's "
+                               "predictor stage 1",
+                     "bytes_per_launch": int(round(launch_bytes.mean())), "avg_launch_us": round(qkv_avg_us, 3),
                      "launches_timed": int(n_ev)},
     }
 

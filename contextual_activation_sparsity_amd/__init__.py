@@ -25,7 +25,7 @@ from ._lib import DejavuError  # noqa: F401
 
 __all__ = ["Dims", "LayerWeights", "PredictorWeights", "workspace", "stack_workspace", "dv_predict",
            "dv_topk", "dv_sparse_mlp", "dv_sparse_attn", "dv_layer_step", "dv_lookahead_stack",
-           "dv_workspace_bytes", "dv_stack_workspace_bytes", "require_gpu", "DejavuError"]
+           "dv_workspace_bytes", "dv_stack_workspace_bytes", "dv_topk_workspace_bytes", "require_gpu", "DejavuError"]
 
 _DT = {"f32": (_lib.DV_F32, torch.float32), "f16": (_lib.DV_F16, torch.float16)}
 
@@ -104,6 +104,10 @@ def dv_workspace_bytes(dims: Dims, B: int, k: int, kh: int) -> int:
     return int(_lib.lib().dv_workspace_bytes(ctypes.byref(d), B, k, kh))
 
 
+def dv_topk_workspace_bytes(B: int, n: int) -> int:
+    return int(_lib.lib().dv_topk_workspace_bytes(B, n))
+
+
 def dv_stack_workspace_bytes(dims: Dims, B: int, k: int, kh: int) -> int:
     d = dims.c()
     return int(_lib.lib().dv_stack_workspace_bytes(ctypes.byref(d), B, k, kh))
@@ -140,6 +144,8 @@ def dv_predict(dims: Dims, pred: PredictorWeights, x_pred: torch.Tensor, s_mlp: 
 def dv_topk(scores: torch.Tensor, k: int, idx: torch.Tensor, ws: Optional[torch.Tensor] = None,
             stream=None) -> None:
     B, n = scores.shape
+    if ws is None and k > 0:
+        ws = _alloc_ws(dv_topk_workspace_bytes(B, n), scores.device)
     wp, wn = _ws(ws)
     st = _lib.lib().dv_topk(_ptr(scores), B, n, k, _ptr(idx), wp, wn, _stream(stream))
     _lib.check("dv_topk", st)

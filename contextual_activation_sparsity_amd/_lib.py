@@ -71,6 +71,7 @@ SIGNATURES = {
                                      c_void_p]),
     "dv_workspace_bytes": (c_size_t, [ctypes.POINTER(DvDims), c_int32, c_int32, c_int32]),
     "dv_stack_workspace_bytes": (c_size_t, [ctypes.POINTER(DvDims), c_int32, c_int32, c_int32]),
+    "dv_topk_workspace_bytes": (c_size_t, [c_int32, c_int32]),
     "dv_timing_start": (c_int32, [c_int32]),
     "dv_timing_stop": (c_int32, [ctypes.POINTER(ctypes.c_float), c_int32]),
     "dv_status_str": (ctypes.c_char_p, [c_int32]),

@@ -126,7 +126,7 @@ dv_status check_pred(const dv_predictor* P) {
 // Workspace layout (sized with the largest tiling any device can pick).
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t z, s_mlp, s_head, idx, heads, qkv, apart, o, h1, u, part, total;
+  size_t z, s_mlp, s_head, idx, heads, qkv, apart, o, h1, u, part, tk_mlp, tk_head, total;
   int max_chunks;
 };
 
@@ -150,6 +150,8 @@ Layout layout_of(const dv_dims* d, int B, int k, int kh) {
   L.h1 = take(f * Bz * d->d_model);
   L.u = take(f * Bz * k);
   L.part = take(f * Bz * dv::rowaxpy_max_rg() * d->d_model);
+  L.tk_mlp = take(dv::topk_ws_bytes(B, d->d_ffn));
+  L.tk_head = take(dv::topk_ws_bytes(B, d->n_heads));
   L.total = off;
   return L;
 }
@@ -190,7 +192,11 @@ TimingHook g_timing;
 dv_status run_rowdot(dv::RowDotArgs& a, bool f16, int B, int cus, hipStream_t st, int tag = 0) {
   int tpr = 0, ch = 0;
   if (!dv::rowdot_plan(a.d, f16, &tpr, &ch)) return fail(DV_ERR_DIMS, "row length %d unsupported", a.d);
-  for (int i = 0; i < a.nseg; ++i) a.seg[i].blocks = dv::rowdot_blocks_for(a.seg[i].n_out, tpr, ch, cus);
+  if (a.nseg < 1 || a.nseg > dv::kRowdotMaxSeg) return fail(DV_ERR_DIMS, "internal: %d row-dot segments", a.nseg);
+  long long total = 0;
+  for (int i = 0; i < a.nseg; ++i) total += a.seg[i].n_out;
+  const int per_slot = dv::rowdot_rows_per_slot(total, tpr, ch, cus);
+  for (int i = 0; i < a.nseg; ++i) a.seg[i].blocks = dv::rowdot_blocks_for(a.seg[i].n_out, tpr, per_slot);
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (tag == 1 && g_timing.active) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
@@ -204,15 +210,31 @@ dv_status run_rowdot(dv::RowDotArgs& a, bool f16, int B, int cus, hipStream_t st
   return DV_OK;
 }
 
+// Predictor stage 1 as two row-dot segments: z[b] = [P1_mlp; P1_head] . x[b] (no norm).
+void predict_stage1_segs(const dv_dims* d, const dv_predictor* P, const float* x, float* z, dv::RowDotSeg* out) {
+  const int rm = d->rank_mlp, rh = d->rank_head, D = d->d_model;
+  out[0] = seg_of(P->p1_mlp, D, rm, 1, rm, nullptr, 0, x, D, nullptr, nullptr, z, rm + rh, 0);
+  out[1] = seg_of(P->p1_head, D, rh, 1, rh, nullptr, 0, x, D, nullptr, nullptr, z + rm, rm + rh, 0);
+}
+
+dv_status run_predict_stage2(const dv_dims* d, const dv_predictor* P, int B, float* s_mlp, float* s_head,
+                             const float* z, int cus, hipStream_t st);
+
 dv_status run_predict(const dv_dims* d, const dv_predictor* P, const float* x, int B, float* s_mlp,
                       float* s_head, float* z, int cus, hipStream_t st) {
   const bool f16 = is_f16(d);
-  const int rm = d->rank_mlp, rh = d->rank_head, D = d->d_model;
   dv::RowDotArgs a{};
-  a.nseg = 2; a.d = D; a.eps = 0.f;
-  a.seg[0] = seg_of(P->p1_mlp, D, rm, 1, rm, nullptr, 0, x, D, nullptr, nullptr, z, rm + rh, 0);
-  a.seg[1] = seg_of(P->p1_head, D, rh, 1, rh, nullptr, 0, x, D, nullptr, nullptr, z + rm, rm + rh, 0);
+  a.nseg = 2; a.d = d->d_model; a.eps = 0.f;
+  predict_stage1_segs(d, P, x, z, a.seg);
   DV_TRY(run_rowdot(a, f16, B, cus, st));
+  return run_predict_stage2(d, P, B, s_mlp, s_head, z, cus, st);
+}
+
+// Predictor stage 2: s_mlp[b] = P2_mlp . z_mlp[b], s_head[b] = P2_head . z_head[b].
+dv_status run_predict_stage2(const dv_dims* d, const dv_predictor* P, int B, float* s_mlp, float* s_head,
+                             const float* z, int cus, hipStream_t st) {
+  const bool f16 = is_f16(d);
+  const int rm = d->rank_mlp, rh = d->rank_head;
   dv::RowDotSeg sm = seg_of(P->p2_mlp, rm, d->d_ffn, 1, d->d_ffn, nullptr, 0, z, rm + rh, nullptr, nullptr,
                             s_mlp, d->d_ffn, 0);
   dv::RowDotSeg sh = seg_of(P->p2_head, rh, d->n_heads, 1, d->n_heads, nullptr, 0, z + rm, rm + rh, nullptr,
@@ -233,11 +255,11 @@ dv_status run_predict(const dv_dims* d, const dv_predictor* P, const float* x, i
 }
 
 dv_status run_topk2(const float* s_mlp, int F, int k, int32_t* idx, const float* s_head, int H, int kh,
-                    int32_t* heads, int B, hipStream_t st) {
+                    int32_t* heads, int B, void* ws_mlp, void* ws_head, hipStream_t st) {
   dv::TopkArgs t{};
   t.nprob = 2;
-  t.p[0] = {s_mlp, F, k, idx};
-  t.p[1] = {s_head, H, kh, heads};
+  t.p[0] = {s_mlp, F, k, idx, dv::topk_ws_carve(ws_mlp, B, F)};
+  t.p[1] = {s_head, H, kh, heads, dv::topk_ws_carve(ws_head, B, H)};
   DV_HIP(dv::launch_topk(t, B, st));
   return DV_OK;
 }
@@ -246,19 +268,22 @@ dv_status run_topk2(const float* s_mlp, int F, int k, int32_t* idx, const float*
 dv_status run_attn(const dv_dims* d, const dv_layer* Lw, const float* x, const float* norm_g, int B,
                    const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* y,
                    const float* resid, const Layout& L, void* ws, int cus, hipStream_t st,
-                   hipEvent_t ev_after_qkv = nullptr) {
+                   hipEvent_t ev_after_qkv = nullptr, const dv::RowDotSeg* extra = nullptr, int n_extra = 0) {
   const bool f16 = is_f16(d);
   const int D = d->d_model, dh = d->head_dim, H = d->n_heads;
   float* qkv = at<float>(ws, L.qkv);
   float* o = at<float>(ws, L.o);
-  if (kh == 0 && ev_after_qkv) DV_HIP(hipEventRecord(ev_after_qkv, st));
+  // Independent rows of the same length (the next layer's predictor stage 1) ride in the
+  // q/k/v launch as further segments.
+  dv::RowDotArgs a{};
+  a.nseg = 0; a.d = D; a.eps = 1e-5f;
+  if (kh > 0)
+    a.seg[a.nseg++] = seg_of(Lw->wqkv, D, kh * 3 * dh, 3 * dh, H, heads, kh, x, D, norm_g, Lw->bqkv, qkv,
+                             (long long)kh * 3 * dh, 0);
+  for (int i = 0; i < n_extra; ++i) a.seg[a.nseg++] = extra[i];
+  if (a.nseg > 0) DV_TRY(run_rowdot(a, f16, B, cus, st, /*tag=*/kh > 0 ? 1 : 0));
+  if (ev_after_qkv) DV_HIP(hipEventRecord(ev_after_qkv, st));
   if (kh > 0) {
-    dv::RowDotArgs a{};
-    a.nseg = 1; a.d = D; a.eps = 1e-5f;
-    a.seg[0] = seg_of(Lw->wqkv, D, kh * 3 * dh, 3 * dh, H, heads, kh, x, D, norm_g, Lw->bqkv, qkv,
-                      (long long)kh * 3 * dh, 0);
-    DV_TRY(run_rowdot(a, f16, B, cus, st, /*tag=*/1));
-    if (ev_after_qkv) DV_HIP(hipEventRecord(ev_after_qkv, st));
     dv::AttnArgs at_{};
     at_.qkv = qkv; at_.heads = heads; at_.kh = kh; at_.n_heads = H; at_.dh = dh; at_.t_past = t_past;
     at_.t_max = d->t_max; at_.k_cache = kc; at_.v_cache = vc; at_.partial = at<float>(ws, L.apart);
@@ -302,9 +327,11 @@ dv_status run_mlp(const dv_dims* d, const dv_layer* Lw, const float* x, const fl
 
 dv_status run_layer(const dv_dims* d, const dv_layer* Lw, const float* x, int B, const int32_t* idx, int k,
                     const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* x_out,
-                    const Layout& L, void* ws, int cus, hipStream_t st, hipEvent_t ev_after_qkv = nullptr) {
+                    const Layout& L, void* ws, int cus, hipStream_t st, hipEvent_t ev_after_qkv = nullptr,
+                    const dv::RowDotSeg* extra = nullptr, int n_extra = 0) {
   float* h1 = at<float>(ws, L.h1);
-  DV_TRY(run_attn(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, t_past, h1, x, L, ws, cus, st, ev_after_qkv));
+  DV_TRY(run_attn(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, t_past, h1, x, L, ws, cus, st, ev_after_qkv, extra,
+                  n_extra));
   DV_TRY(run_mlp(d, Lw, h1, Lw->g2, B, idx, k, x_out, h1, L, ws, cus, st));
   return DV_OK;
 }
@@ -422,18 +449,23 @@ dv_status dv_predict(const dv_dims* dims, const dv_predictor* pred, const float*
   return run_predict(dims, pred, x_pred, B, s_mlp, s_head, at<float>(ws, L.z), di->cus, stream);
 }
 
+size_t dv_topk_workspace_bytes(int32_t B, int32_t n) {
+  if (B <= 0 || n <= 0 || n > dv::kTopkMaxChunks * dv::kTopkChunk) return 0;
+  return align256(dv::topk_ws_bytes(B, n));
+}
+
 dv_status dv_topk(const float* scores, int32_t B, int32_t n, int32_t k, int32_t* idx, void* ws,
                   size_t ws_bytes, hipStream_t stream) {
-  (void)ws; (void)ws_bytes;
   if (B <= 0 || n <= 0) return fail(DV_ERR_DIMS, "B and n must be positive");
-  if (n > 65536) return fail(DV_ERR_DIMS, "n must be <= 65536");
+  if (n > dv::kTopkMaxChunks * dv::kTopkChunk) return fail(DV_ERR_DIMS, "n must be <= 65536");
   if (k < 0 || k > n) return fail(DV_ERR_K, "k=%d outside [0, %d]", k, n);
   if (scores == nullptr) return fail(DV_ERR_NULL, "scores is NULL");
   if (k > 0 && idx == nullptr) return fail(DV_ERR_NULL, "idx is NULL");
   if (k == 0) return DV_OK;
+  DV_TRY(check_ws(ws, ws_bytes, dv_topk_workspace_bytes(B, n)));
   dv::TopkArgs t{};
   t.nprob = 1;
-  t.p[0] = {scores, n, k, idx};
+  t.p[0] = {scores, n, k, idx, dv::topk_ws_carve(ws, B, n)};
   t.p[1] = t.p[0];
   DV_HIP(dv::launch_topk(t, B, stream));
   return DV_OK;
@@ -501,7 +533,7 @@ dv_status dv_layer_step(const dv_dims* dims, const dv_layer* layer, const dv_pre
     DV_TRY(run_predict(dims, pred, x_pred, B, at<float>(ws, L.s_mlp), at<float>(ws, L.s_head),
                        at<float>(ws, L.z), di->cus, stream));
     DV_TRY(run_topk2(at<float>(ws, L.s_mlp), dims->d_ffn, k, io, at<float>(ws, L.s_head), dims->n_heads, kh,
-                     ho, B, stream));
+                     ho, B, at<char>(ws, L.tk_mlp), at<char>(ws, L.tk_head), stream));
     idx = io;
     heads = ho;
   } else {
@@ -564,32 +596,36 @@ dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const 
   auto sel_heads = [&](int l) -> int32_t* {
     return heads_out ? heads_out + (size_t)l * B * kh : ring_heads[l % 2];
   };
-  auto predict_sets = [&](int l, const float* hin, void* w, hipStream_t st) -> dv_status {
-    DV_TRY(run_predict(dims, &preds[l], hin, B, at<float>(w, L.s_mlp), at<float>(w, L.s_head), at<float>(w, L.z),
-                       cus, st));
+  auto topk_sets = [&](int l, void* w, hipStream_t st) -> dv_status {
     return run_topk2(at<float>(w, L.s_mlp), dims->d_ffn, k, sel_idx(l), at<float>(w, L.s_head), dims->n_heads,
-                     kh, sel_heads(l), B, st);
+                     kh, sel_heads(l), B, at<char>(w, L.tk_mlp), at<char>(w, L.tk_head), st);
   };
 
   const bool two = side_stream != stream;
+  hipStream_t st_side = two ? side_stream : stream;
   if (h_all) DV_HIP(hipMemcpyAsync(h_all, x, vecb, hipMemcpyDeviceToDevice, stream));
   // Layer 0's sets come from the stack input, before any layer runs.
-  DV_TRY(predict_sets(0, h_in(0), ws, stream));
+  DV_TRY(run_predict(dims, &preds[0], h_in(0), B, at<float>(ws, L.s_mlp), at<float>(ws, L.s_head),
+                     at<float>(ws, L.z), cus, stream));
+  DV_TRY(topk_sets(0, ws, stream));
   for (int l = 0; l < n_layers; ++l) {
-    if (l + 1 < n_layers) {
-      // Sets of layer l+1 from the input of layer l, on the side stream while layer l runs.
-      if (two) {
-        DV_HIP(hipEventRecord(di->ev_in, stream));
-        DV_HIP(hipStreamWaitEvent(side_stream, di->ev_in, 0));
-        DV_TRY(predict_sets(l + 1, h_in(l), ws_side, side_stream));
-        DV_HIP(hipEventRecord(di->ev_sel[(l + 1) % 2], side_stream));
-      } else {
-        DV_TRY(predict_sets(l + 1, h_in(l), ws_side, stream));
-      }
-    }
     if (two && l >= 1) DV_HIP(hipStreamWaitEvent(stream, di->ev_sel[l % 2], 0));
+    // The sets of layer l+1 are predicted from the input of layer l: predictor stage 1 reads
+    // the same vector as layer l's q/k/v projection and rides in that launch; stage 2 and the
+    // top-k then run on the side stream while layer l finishes.
+    const bool ahead = l + 1 < n_layers;
+    dv::RowDotSeg p1[2];
+    if (ahead) predict_stage1_segs(dims, &preds[l + 1], h_in(l), at<float>(ws_side, L.z), p1);
     DV_TRY(run_layer(dims, &layers[l], h_in(l), B, sel_idx(l), k, sel_heads(l), kh, k_caches[l], v_caches[l],
-                     t_past, h_outp(l), L, ws, cus, stream));
+                     t_past, h_outp(l), L, ws, cus, stream, (ahead && two) ? di->ev_in : nullptr,
+                     ahead ? p1 : nullptr, ahead ? 2 : 0));
+    if (ahead) {
+      if (two) DV_HIP(hipStreamWaitEvent(st_side, di->ev_in, 0));
+      DV_TRY(run_predict_stage2(dims, &preds[l + 1], B, at<float>(ws_side, L.s_mlp), at<float>(ws_side, L.s_head),
+                                at<float>(ws_side, L.z), cus, st_side));
+      DV_TRY(topk_sets(l + 1, ws_side, st_side));
+      if (two) DV_HIP(hipEventRecord(di->ev_sel[(l + 1) % 2], st_side));
+    }
   }
   if (h_all && y != h_all + (size_t)n_layers * B * D)
     DV_HIP(hipMemcpyAsync(y, h_all + (size_t)n_layers * B * D, vecb, hipMemcpyDeviceToDevice, stream));

@@ -29,8 +29,9 @@ struct RowDotSeg {
   int blocks;               // blocks (grid.x) given to this segment
 };
 
+constexpr int kRowdotMaxSeg = 3;
 struct RowDotArgs {
-  RowDotSeg seg[2];
+  RowDotSeg seg[kRowdotMaxSeg];   // independent row sets sharing the row length d
   int nseg;
   int d;                    // row length (elements), shared by both segments
   float eps;
@@ -39,7 +40,10 @@ struct RowDotArgs {
 // Chooses the tiling for row length d (elements) and storage type; returns false if d is
 // not supported. rows_in_flight: rows one block keeps loading at once.
 bool rowdot_plan(int d, bool f16, int* tpr, int* ch);
-int rowdot_blocks_for(int n_out, int tpr, int ch, int cus);
+// Rows per row-slot so that all segments together fill the chip once; blocks of a segment
+// with n_out rows at that depth.
+int rowdot_rows_per_slot(long long total_rows, int tpr, int ch, int cus);
+int rowdot_blocks_for(int n_out, int tpr, int per_slot);
 hipError_t launch_rowdot(const RowDotArgs& a, bool f16, int B, hipStream_t s, int tag,
                          hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 
@@ -95,18 +99,31 @@ bool attn_plan(int dh, bool f16, int t_total, int kh, int B, int cus, int* chunk
 hipError_t launch_attn(const AttnArgs& a, bool f16, int B, hipStream_t s);
 
 // ---------------------------------------------------------------------------
-// Exact top-k by radix select (one block per row and problem).
+// Exact top-k by radix select over many CUs (three kernels, see k_topk.hip).
 // ---------------------------------------------------------------------------
+constexpr int kTopkChunk = 4096;     // scores per chunk block
+constexpr int kTopkMaxChunks = 16;   // n <= 65536
+struct TopkWs {                      // per problem, rows b = 0..B-1 (caller workspace)
+  unsigned* part;                    // [B][chunks][2048] chunk histograms of bits 31..21
+  unsigned* bits;                    // [B][chunks * 128] bitmap of selected positions
+  unsigned* ckey;                    // [B][chunks][4096] candidate keys of the threshold bin
+  unsigned* cidx;                    // [B][chunks][4096] their positions
+  unsigned* ccnt;                    // [B][chunks] candidates per chunk
+  unsigned* sel;                     // [B][4] threshold bin, keys above it, keys in it
+};
 struct TopkProb {
   const float* scores;      // [B][n]
   int n;
   int k;
   int32_t* out;             // [B][k]
+  TopkWs ws;
 };
 struct TopkArgs {
   TopkProb p[2];
   int nprob;
 };
+size_t topk_ws_bytes(int B, int n);              // scratch of one problem
+TopkWs topk_ws_carve(void* base, int B, int n);  // base: 256-byte aligned, topk_ws_bytes long
 hipError_t launch_topk(const TopkArgs& a, int B, hipStream_t s);
 
 }  // namespace dv

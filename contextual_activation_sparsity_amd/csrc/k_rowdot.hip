@@ -24,10 +24,13 @@ constexpr int kRowdotBlock = 256;
 #define DV_ROWDOT_BPC_BIG 2  // target resident blocks per CU for long rows (>= 5 chunks/thread)
 #endif
 #ifndef DV_ROWDOT_BPC
-#define DV_ROWDOT_BPC 4      // target resident blocks per CU otherwise
+#define DV_ROWDOT_BPC 2      // target resident blocks per CU otherwise
 #endif
 #ifndef DV_ROWDOT_RBIG
 #define DV_ROWDOT_RBIG 4     // rows in flight per row-slot when a thread holds >= 5 chunks
+#endif
+#ifndef DV_ROWDOT_WAVES_PER_EU
+#define DV_ROWDOT_WAVES_PER_EU 1  // lower bound on resident waves per SIMD the registers must allow
 #endif
 
 __host__ __device__ constexpr int rowdot_rows_in_flight(int ch) {
@@ -36,7 +39,8 @@ __host__ __device__ constexpr int rowdot_rows_in_flight(int ch) {
 
 // TAG only separates launch sites in profiles (1 = head-sparse q/k/v projection).
 template <typename WT, int TPR, int CH, int TAG>
-__global__ __launch_bounds__(kRowdotBlock) void rowdot_kernel(RowDotArgs a) {
+__global__ __launch_bounds__(kRowdotBlock) __attribute__((amdgpu_waves_per_eu(DV_ROWDOT_WAVES_PER_EU)))
+void rowdot_kernel(RowDotArgs a) {
   constexpr int VEC = Vec<WT>::N;
   constexpr int SLOTS = kRowdotBlock / TPR;
   constexpr int R = rowdot_rows_in_flight(CH);
@@ -48,9 +52,17 @@ __global__ __launch_bounds__(kRowdotBlock) void rowdot_kernel(RowDotArgs a) {
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
   int bx = blockIdx.x;
-  const bool second = a.nseg > 1 && bx >= a.seg[0].blocks;
-  if (second) bx -= a.seg[0].blocks;
-  const RowDotSeg S = second ? a.seg[1] : a.seg[0];
+  int si = 0;
+  if (a.nseg > 1 && bx >= a.seg[0].blocks) {
+    bx -= a.seg[0].blocks;
+    si = 1;
+    if (a.nseg > 2 && bx >= a.seg[1].blocks) {
+      bx -= a.seg[1].blocks;
+      si = 2;
+    }
+  }
+  static_assert(kRowdotMaxSeg == 3, "segment selection covers three segments");
+  const RowDotSeg S = si == 0 ? a.seg[0] : (si == 1 ? a.seg[1] : a.seg[2]);
 
   const int slot = tid / TPR;
   const int lr = tid % TPR;
@@ -203,7 +215,9 @@ __global__ __launch_bounds__(kRowdotBlock) void rowdot_kernel(RowDotArgs a) {
 // host side: tiling choice and dispatch
 // --------------------------------------------------------------------------
 
-static const int kTprs[] = {256, 128, 64, 32};
+// Among tilings with the same lane utilisation the one with the fewest threads per row wins:
+// rows shared by at most one wave reduce with shuffles only (no LDS round and no barrier).
+static const int kTprs[] = {32, 64, 128, 256};
 
 static bool ch_supported(int ch) { return ch == 1 || ch == 2 || ch == 3 || ch == 4 || ch == 5 || ch == 6 || ch == 8; }
 
@@ -222,12 +236,17 @@ bool rowdot_plan(int d, bool f16, int* tpr, int* ch) {
   return best > 0.0;
 }
 
-int rowdot_blocks_for(int n_out, int tpr, int ch, int cus) {
-  if (n_out <= 0) return 1;
+int rowdot_rows_per_slot(long long total_rows, int tpr, int ch, int cus) {
   const int slots = kRowdotBlock / tpr;
   const long long target = (long long)cus * (ch >= 5 ? DV_ROWDOT_BPC_BIG : DV_ROWDOT_BPC);
-  const long long per_slot = ((long long)n_out + target * slots - 1) / (target * slots);
-  long long blocks = ((long long)n_out + per_slot * slots - 1) / (per_slot * slots);
+  if (total_rows < 1) total_rows = 1;
+  return (int)((total_rows + target * slots - 1) / (target * slots));
+}
+
+int rowdot_blocks_for(int n_out, int tpr, int per_slot) {
+  if (n_out <= 0) return 1;
+  const int slots = kRowdotBlock / tpr;
+  long long blocks = ((long long)n_out + (long long)per_slot * slots - 1) / ((long long)per_slot * slots);
   if (blocks < 1) blocks = 1;
   return (int)blocks;
 }

@@ -6,19 +6,18 @@
 // onto +0.0 and every NaN mapped to 0 (below -inf). The k largest keys win; among equal
 // keys the lower index wins. Output is the selected indices in ascending order.
 //
-// One block of 1024 threads per (row, problem); one CU retires 64 lane-ops per clock, so
-// the design minimises sweeps over the keys:
-//  1. Coalesced striped load (element t + 1024 j goes to thread t, register j), fused with
-//     the histogram of the top 11 key bits (LDS, four copies to spread atomics). A scan of
-//     the 2048 bins gives the bin holding the k-th largest key and how many keys above it
-//     are already taken.
-//  2. The keys of that bin are compacted into LDS (typically 1-3 % of n) and the remaining
-//     21 bits are resolved there (11 + 10 bit passes). If the bin holds more keys than the
-//     LDS list, the two passes run over the registers instead.
-//  3. The threshold key tau and the number r of keys equal to tau still needed are known.
-//     Each wave ballots "key > tau" and "key == tau" for each register row; one block scan
-//     of the per-(row, wave) counts in index order gives every selected element its output
-//     position, and a tie is taken iff fewer than r ties precede it in index order.
+// A radix select spread over many CUs. Three kernels, and no block ever waits on another
+// (the kernel boundaries order them):
+//  1. topk_hist_kernel: one block per 4096-score chunk writes the chunk's histogram of the
+//     top 11 key bits.
+//  2. topk_classify_kernel: every chunk block sums the chunk histograms, finds the bin d0
+//     holding the k-th largest key, and sorts its own scores into "above d0" (ballots
+//     straight into a bitmap of selected positions) and "in d0" (candidates, compacted in
+//     index order into the chunk's list).
+//  3. topk_finish_kernel: one block per row gathers the candidates (typically 1-3 % of n),
+//     resolves the remaining 21 key bits with two more histogram passes, takes the ties at
+//     the threshold key in index order, sets their bits, and turns the bitmap into the
+//     ascending index list with one block scan of per-word popcounts.
 // Integer-exact and unique.
 #include "dv_device.h"
 #include "dv_kernels.h"
@@ -32,234 +31,348 @@ __device__ __forceinline__ unsigned order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kTopkBlock = 1024;
-constexpr int kTopkWaves = kTopkBlock / kWave;
-constexpr int kTopkBins = 2048;   // 11-bit digits: bits 31..21, then 20..10, then 9..0
-constexpr int kTopkCopies = 4;    // histogram copies (wave w uses copy w % 4)
-constexpr int kTopkCand = 4096;   // LDS list for the keys of the threshold bin
+constexpr int kTkBlock = 1024;
+constexpr int kTkWaves = kTkBlock / kWave;
+constexpr int kTkEpt = kTopkChunk / kTkBlock;   // scores per thread per chunk (4)
+constexpr int kTkBins = 2048;                    // 11-bit digits: bits 31..21, 20..10, 9..0
+constexpr int kTkCopies = 2;                     // LDS histogram copies (wave w uses w % 2)
+constexpr int kTkCandLds = 8192;                 // candidates resolved from LDS
+static_assert(kTkEpt * kTkBlock == kTopkChunk, "chunk must be a whole number of block sweeps");
+static_assert(kTopkChunk % 64 == 0, "a chunk is whole waves");
 
-// Exclusive scan over the block of two per-thread counts (thread order); also returns the totals.
-__device__ __forceinline__ void block_scan2(unsigned a, unsigned b, unsigned* ea, unsigned* eb,
-                                            unsigned* ta, unsigned* tb, unsigned (*s)[kTopkWaves]) {
+// Exclusive scan over the block of one per-thread count (thread order); also returns the total.
+__device__ __forceinline__ unsigned block_scan(unsigned a, unsigned* total, unsigned* s) {
   const int lane = threadIdx.x % kWave;
   const int w = threadIdx.x / kWave;
-  unsigned ia = a, ib = b;
+  unsigned ia = a;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    const unsigned xa = __shfl_up(ia, off, kWave);
-    const unsigned xb = __shfl_up(ib, off, kWave);
-    if (lane >= off) { ia += xa; ib += xb; }
+    const unsigned x = __shfl_up(ia, off, kWave);
+    if (lane >= off) ia += x;
   }
-  if (lane == kWave - 1) { s[0][w] = ia; s[1][w] = ib; }
+  if (lane == kWave - 1) s[w] = ia;
   __syncthreads();
-  unsigned pa = 0, pb = 0, sa = 0, sb = 0;
+  unsigned p = 0, t = 0;
 #pragma unroll
-  for (int i = 0; i < kTopkWaves; ++i) {
-    if (i < w) { pa += s[0][i]; pb += s[1][i]; }
-    sa += s[0][i]; sb += s[1][i];
+  for (int i = 0; i < kTkWaves; ++i) {
+    if (i < w) p += s[i];
+    t += s[i];
   }
-  *ea = pa + ia - a;
-  *eb = pb + ib - b;
-  *ta = sa;
-  *tb = sb;
+  __syncthreads();
+  *total = t;
+  return p + ia - a;
+}
+
+// Bin of a histogram (nbins <= 2048, thread t holds bins nbins-1-2t and nbins-2-2t, i.e.
+// descending digit order) that holds the krem-th largest key; returns {bin, rank inside it,
+// keys in it} through s_sel. 1 <= krem <= total is required.
+__device__ __forceinline__ void select_bin(unsigned c0, unsigned c1, int nbins, unsigned krem, unsigned* s_sel,
+                                           unsigned* s_scan) {
+  const int t = threadIdx.x;
+  unsigned total;
+  const unsigned before = block_scan(c0 + c1, &total, s_scan);
+  if (before < krem && krem <= before + c0) {
+    s_sel[0] = (unsigned)(nbins - 1 - 2 * t);
+    s_sel[1] = krem - before;
+    s_sel[2] = c0;
+  } else if (before + c0 < krem && krem <= before + c0 + c1) {
+    s_sel[0] = (unsigned)(nbins - 2 - 2 * t);
+    s_sel[1] = krem - before - c0;
+    s_sel[2] = c1;
+  }
   __syncthreads();
 }
 
-// Finds the digit bin holding the krem-th largest key (counting from the top) in a histogram
-// of nbins bins; returns the bin in s_sel[0] and the rank inside it in s_sel[1].
-__device__ __forceinline__ void find_bin(const unsigned (*hist)[kTopkBins], int nbins, unsigned krem,
-                                         unsigned* s_sel, unsigned (*s_scan)[kTopkWaves]) {
-  constexpr int BPT = kTopkBins / kTopkBlock;  // 2 bins per thread, descending digit order
-  const int tid = threadIdx.x;
-  unsigned cnt[BPT], tot = 0;
+__device__ __forceinline__ const TopkProb& prob_of(const TopkArgs& a) {
+  return blockIdx.z == 0 ? a.p[0] : a.p[1];
+}
+
+// 1. per-chunk histograms of bits 31..21 -> part[b][chunk][2048]
+__global__ __launch_bounds__(kTkBlock) void topk_hist_kernel(TopkArgs a) {
+  __shared__ unsigned s_hist[kTkCopies][kTkBins];
+  const TopkProb& P = prob_of(a);
+  const int c = blockIdx.x, b = blockIdx.y, n = P.n, tid = threadIdx.x;
+  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+  if (P.k <= 0 || P.k >= n || c >= nch) return;
+  const float* sc = P.scores + (long long)b * n;
+  for (int i = tid; i < kTkCopies * kTkBins; i += kTkBlock) (&s_hist[0][0])[i] = 0u;
+  unsigned key[kTkEpt];
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    const int bin = nbins - 1 - (tid * BPT + j);
-    unsigned c = 0;
-    if (bin >= 0)
-#pragma unroll
-      for (int q = 0; q < kTopkCopies; ++q) c += hist[q][bin];
-    cnt[j] = c;
-    tot += c;
+  for (int j = 0; j < kTkEpt; ++j) {
+    const int i = c * kTopkChunk + j * kTkBlock + tid;
+    key[j] = i < n ? order_key(sc[i]) : 0u;
   }
-  unsigned before, unused, t0, t1;
-  block_scan2(tot, 0u, &before, &unused, &t0, &t1, s_scan);
+  __syncthreads();
+  const int copy = (tid / kWave) % kTkCopies;
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    if (before < krem && krem <= before + cnt[j]) {
-      s_sel[0] = (unsigned)(nbins - 1 - (tid * BPT + j));
-      s_sel[1] = krem - before;
+  for (int j = 0; j < kTkEpt; ++j) {
+    const int i = c * kTopkChunk + j * kTkBlock + tid;
+    if (i < n) atomicAdd(&s_hist[copy][key[j] >> 21], 1u);   // padding is not counted
+  }
+  __syncthreads();
+  unsigned* part = P.ws.part + ((long long)b * nch + c) * kTkBins;
+  for (int bin = tid; bin < kTkBins; bin += kTkBlock) {
+    unsigned v = 0;
+#pragma unroll
+    for (int q = 0; q < kTkCopies; ++q) v += s_hist[q][bin];
+    part[bin] = v;
+  }
+}
+
+// 2. threshold bin from the summed histogram; above-bin bits and in-bin candidates per chunk
+__global__ __launch_bounds__(kTkBlock) void topk_classify_kernel(TopkArgs a) {
+  __shared__ unsigned s_scan[kTkWaves];
+  __shared__ unsigned s_sel[3];
+  __shared__ unsigned s_cnt[kTkEpt * kTkWaves];
+  const TopkProb& P = prob_of(a);
+  const int c = blockIdx.x, b = blockIdx.y, n = P.n, k = P.k, tid = threadIdx.x;
+  const int lane = tid % kWave, w = tid / kWave;
+  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+  if (k <= 0 || k >= n || c >= nch) return;
+  const float* sc = P.scores + (long long)b * n;
+  // every load of the block is issued before the first one is used
+  unsigned key[kTkEpt];
+#pragma unroll
+  for (int j = 0; j < kTkEpt; ++j) {
+    const int i = c * kTopkChunk + j * kTkBlock + tid;
+    key[j] = order_key(sc[min(i, n - 1)]);
+  }
+  // thread t owns bins 2047-2t (c0) and 2046-2t (c1); stored pairs are (2046-2t, 2047-2t)
+  const unsigned* part = P.ws.part + (long long)b * nch * kTkBins;
+  uint2 pv[kTopkMaxChunks];
+#pragma unroll
+  for (int q = 0; q < kTopkMaxChunks; ++q)   // all chunk loads in flight together
+    pv[q] = q < nch ? *reinterpret_cast<const uint2*>(part + (long long)q * kTkBins + (kTkBins - 2 - 2 * tid))
+                    : make_uint2(0u, 0u);
+  unsigned c0 = 0, c1 = 0;
+#pragma unroll
+  for (int q = 0; q < kTopkMaxChunks; ++q) {
+    c1 += pv[q].x;
+    c0 += pv[q].y;
+  }
+  select_bin(c0, c1, kTkBins, (unsigned)k, s_sel, s_scan);
+  const unsigned d0 = s_sel[0];
+  if (c == 0 && tid == 0) {   // the threshold bin, keys above it, keys in it
+    unsigned* sel = P.ws.sel + (long long)b * 4;
+    sel[0] = d0;
+    sel[1] = (unsigned)k - s_sel[1];
+    sel[2] = s_sel[2];
+    sel[3] = 0u;
+  }
+  // above-bin positions: each (sweep j, wave w) covers 64 consecutive scores = 2 bitmap words
+  unsigned* bits = P.ws.bits + (long long)b * nch * (kTopkChunk / 32);
+  bool eq[kTkEpt];
+#pragma unroll
+  for (int j = 0; j < kTkEpt; ++j) {
+    const int i = c * kTopkChunk + j * kTkBlock + tid;
+    const unsigned dg = key[j] >> 21;
+    const bool ok = i < n;
+    const unsigned long long gm = __ballot(ok && dg > d0);
+    eq[j] = ok && dg == d0;
+    const unsigned long long em = __ballot(eq[j]);
+    if (lane == 0) {
+      *reinterpret_cast<uint2*>(bits + c * (kTopkChunk / 32) + j * (kTkBlock / 32) + w * 2) =
+          make_uint2((unsigned)gm, (unsigned)(gm >> 32));
+      s_cnt[j * kTkWaves + w] = (unsigned)__popcll(em);
     }
-    before += cnt[j];
   }
   __syncthreads();
+  // exclusive scan of the (sweep, wave) candidate counts in index order, by wave 0
+  if (w == 0) {
+    const unsigned v = lane < kTkEpt * kTkWaves ? s_cnt[lane] : 0u;
+    unsigned s = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const unsigned x = __shfl_up(s, off, kWave);
+      if (lane >= off) s += x;
+    }
+    if (lane < kTkEpt * kTkWaves) s_cnt[lane] = s - v;
+    if (lane == kWave - 1) P.ws.ccnt[(long long)b * nch + c] = s;
+  }
+  static_assert(kTkEpt * kTkWaves <= kWave, "one wave scans the candidate counts");
+  __syncthreads();
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  unsigned* ckey = P.ws.ckey + (long long)b * nch * kTopkChunk + c * kTopkChunk;
+  unsigned* cidx = P.ws.cidx + (long long)b * nch * kTopkChunk + c * kTopkChunk;
+#pragma unroll
+  for (int j = 0; j < kTkEpt; ++j) {
+    const unsigned long long em = __ballot(eq[j]);
+    if (eq[j]) {
+      const unsigned pos = s_cnt[j * kTkWaves + w] + (unsigned)__popcll(em & below);
+      ckey[pos] = key[j];
+      cidx[pos] = (unsigned)(c * kTopkChunk + j * kTkBlock + tid);
+    }
+  }
 }
 
-template <int KPT>
-__global__ __launch_bounds__(kTopkBlock) void topk_kernel(TopkArgs a) {
-  __shared__ unsigned s_hist[kTopkCopies][kTopkBins];
-  __shared__ unsigned s_cand[kTopkCand];
-  __shared__ unsigned s_cnt[2][KPT][kTopkWaves];
-  __shared__ unsigned s_sel[2];
-  __shared__ unsigned s_ncand;
-  __shared__ unsigned s_scan[2][kTopkWaves];
-
-  const TopkProb& P = blockIdx.y == 0 ? a.p[0] : a.p[1];
-  const int b = blockIdx.x;
-  const int n = P.n;
-  const int k = P.k;
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int w = tid / kWave;
-  const int copy = w % kTopkCopies;
+// 3. resolve the threshold bin, take the ties in index order, bitmap -> ascending list
+__global__ __launch_bounds__(kTkBlock) void topk_finish_kernel(TopkArgs a) {
+  __shared__ unsigned s_bits[kTopkMaxChunks * (kTopkChunk / 32)];
+  __shared__ unsigned s_hist[kTkCopies][kTkBins];
+  __shared__ unsigned s_ck[kTkCandLds];
+  __shared__ unsigned s_ci[kTkCandLds];
+  __shared__ unsigned s_scan[kTkWaves];
+  __shared__ unsigned s_sel[3];
+  __shared__ unsigned s_pre[kTopkMaxChunks + 1];
+  __shared__ unsigned s_tk[2];
+  const TopkProb& P = prob_of(a);
+  const int b = blockIdx.x, n = P.n, k = P.k, tid = threadIdx.x;
+  const int copy = (tid / kWave) % kTkCopies;
   if (k <= 0) return;
   int32_t* out = P.out + (long long)b * k;
   if (k >= n) {
-    for (int i = tid; i < n; i += kTopkBlock) out[i] = i;
+    for (int i = tid; i < n; i += kTkBlock) out[i] = i;
     return;
   }
-  const float* sc = P.scores + (long long)b * n;
+  const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+  const int nwords = nch * (kTopkChunk / 32);
+  const unsigned* sel = P.ws.sel + (long long)b * 4;
+  const unsigned* ccnt = P.ws.ccnt + (long long)b * nch;
+  const unsigned* gbits = P.ws.bits + (long long)b * nwords;
+  const unsigned* gck = P.ws.ckey + (long long)b * nch * kTopkChunk;
+  const unsigned* gci = P.ws.cidx + (long long)b * nch * kTopkChunk;
 
-  for (int i = tid; i < kTopkCopies * kTopkBins; i += kTopkBlock) (&s_hist[0][0])[i] = 0u;
-  if (tid == 0) { s_sel[0] = 0u; s_sel[1] = 1u; s_ncand = 0u; }
-  __syncthreads();
-
-  // 1. coalesced load + histogram of bits 31..21
-  unsigned key[KPT];
-  // branch-free: every load is issued before the first one is consumed
+  // independent loads first: bitmap words, per-chunk candidate counts, the threshold record
+  const unsigned bw0 = tid < nwords ? gbits[tid] : 0u;
+  const unsigned bw1 = tid + kTkBlock < nwords ? gbits[tid + kTkBlock] : 0u;
+  const unsigned cq = tid < nch ? ccnt[tid] : 0u;
+  const unsigned d0 = sel[0];
+  const unsigned above = sel[1];
+  static_assert(2 * kTkBlock >= kTopkMaxChunks * (kTopkChunk / 32), "two bitmap words per thread");
+  if (tid < nwords) s_bits[tid] = bw0;
+  if (tid + kTkBlock < nwords) s_bits[tid + kTkBlock] = bw1;
+  if (tid < kWave) {   // exclusive scan of the chunk counts by wave 0
+    unsigned sc = cq;
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int i = tid + j * kTopkBlock;
-    const float v = sc[min(i, n - 1)];
-    key[j] = order_key(v) & (0u - (unsigned)(i < n));   // arithmetic mask, no branch
+    for (int off = 1; off < kWave; off <<= 1) {
+      const unsigned t = __shfl_up(sc, off, kWave);
+      if (tid >= off) sc += t;
+    }
+    if (tid <= nch) s_pre[tid] = sc - cq;   // s_pre[nch] = total (cq = 0 there)
   }
-  // Positions past n hold key 0 (the NaN key): they lose every comparison and come last by
-  // index, so with k <= n they are never selected and need no further bounds checks.
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    atomicAdd(&s_hist[copy][key[j] >> 21], 1u);
-    __builtin_amdgcn_sched_barrier(0);  // one row at a time: keeps register pressure flat
-  }
+  static_assert(kTopkMaxChunks < kWave, "one wave scans the chunk counts");
   __syncthreads();
-  find_bin(s_hist, kTopkBins, (unsigned)k, s_sel, s_scan);
-  const unsigned d0 = s_sel[0];
-  unsigned krem = s_sel[1];
-  unsigned bin_count = 0;
-#pragma unroll
-  for (int q = 0; q < kTopkCopies; ++q) bin_count += s_hist[q][d0];
-  unsigned prefix = d0 << 21, pmask = 2047u << 21;
-
-  // 2. resolve the low 21 bits among the keys of bin d0
-  const bool compact = bin_count <= (unsigned)kTopkCand;  // block-uniform (padding counts too)
-  if (compact) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      if ((key[j] >> 21) == d0) s_cand[atomicAdd(&s_ncand, 1u)] = key[j];
-      __builtin_amdgcn_sched_barrier(0);
+  const unsigned ncand = s_pre[nch];   // == keys in bin d0
+  const bool in_lds = ncand <= (unsigned)kTkCandLds;   // block-uniform
+  // candidate g (0 <= g < ncand, index order) lives in chunk q at offset g - s_pre[q]
+  auto gpos = [&](unsigned g) -> long long {
+    int q = 0;
+    while (q + 1 < nch && s_pre[q + 1] <= g) ++q;
+    return (long long)q * kTopkChunk + (g - s_pre[q]);
+  };
+  if (in_lds) {
+    for (unsigned g = tid; g < ncand; g += kTkBlock) {
+      const long long p = gpos(g);
+      s_ck[g] = gck[p];
+      s_ci[g] = gci[p];
     }
   }
   __syncthreads();
-  const int ncand = (int)s_ncand;
+  auto cand_key = [&](unsigned g) -> unsigned { return in_lds ? s_ck[g] : gck[gpos(g)]; };
+  auto cand_idx = [&](unsigned g) -> unsigned { return in_lds ? s_ci[g] : gci[gpos(g)]; };
+
+  unsigned krem = (unsigned)k - above;   // 1 <= krem <= ncand
+  unsigned prefix = d0 << 21, pmask = 2047u << 21;
 #pragma unroll
   for (int pass = 1; pass < 3; ++pass) {
     const int shift = pass == 1 ? 10 : 0;
-    const unsigned dmask = pass == 1 ? 2047u : 1023u;
-    for (int i = tid; i < kTopkCopies * kTopkBins; i += kTopkBlock) (&s_hist[0][0])[i] = 0u;
+    const int nb = pass == 1 ? 2048 : 1024;
+    const unsigned dmask = (unsigned)nb - 1u;
+    for (int i = tid; i < kTkCopies * kTkBins; i += kTkBlock) (&s_hist[0][0])[i] = 0u;
     __syncthreads();
-    if (compact) {
-      for (int i = tid; i < ncand; i += kTopkBlock) {
-        const unsigned kv = s_cand[i];
-        if ((kv & pmask) == prefix) atomicAdd(&s_hist[copy][(kv >> shift) & dmask], 1u);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j)
-      {
-        if ((key[j] & pmask) == prefix) atomicAdd(&s_hist[copy][(key[j] >> shift) & dmask], 1u);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (unsigned g = tid; g < ncand; g += kTkBlock) {
+      const unsigned kv = cand_key(g);
+      if ((kv & pmask) == prefix) atomicAdd(&s_hist[copy][(kv >> shift) & dmask], 1u);
     }
     __syncthreads();
-    find_bin(s_hist, (int)dmask + 1, krem, s_sel, s_scan);
+    unsigned h0 = 0, h1 = 0;
+    const int b0 = nb - 1 - 2 * tid, b1 = nb - 2 - 2 * tid;
+#pragma unroll
+    for (int q = 0; q < kTkCopies; ++q) {
+      if (b0 >= 0) h0 += s_hist[q][b0];
+      if (b1 >= 0) h1 += s_hist[q][b1];
+    }
+    select_bin(h0, h1, nb, krem, s_sel, s_scan);
     prefix |= s_sel[0] << shift;
     pmask |= dmask << shift;
     krem = s_sel[1];
   }
-  const unsigned tau = prefix;  // the k-th largest key; krem of the keys equal to it are taken
-  __shared__ unsigned s_tk[3];
-  if (tid == 0) { s_tk[0] = tau; s_tk[1] = krem; s_tk[2] = 0u; }
-
-  // 3. positions in ascending index order from per-(row, wave) ballot counts
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const unsigned long long gm = __ballot(key[j] > tau);
-    const unsigned long long em = __ballot(key[j] == tau);
-    if (lane == 0) {
-      s_cnt[0][j][w] = (unsigned)__popcll(gm);
-      s_cnt[1][j][w] = (unsigned)__popcll(em);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+  // tau = the k-th largest key; krem of the keys equal to tau are taken, lowest index first
+  if (tid == 0) { s_tk[0] = prefix; s_tk[1] = krem; }
+  __syncthreads();
+  const unsigned tau = s_tk[0], take = s_tk[1];
+  unsigned taken = 0;   // ties already taken in earlier sweeps (block-uniform)
+  for (unsigned g0 = 0; g0 < ncand; g0 += kTkBlock) {
+    const unsigned g = g0 + tid;
+    unsigned kv = 0, ix = 0;
+    if (g < ncand) { kv = cand_key(g); ix = cand_idx(g); }
+    const bool gt = g < ncand && kv > tau;
+    const bool eq = g < ncand && kv == tau;
+    unsigned tot;
+    const unsigned rank = taken + block_scan(eq ? 1u : 0u, &tot, s_scan);
+    if (gt || (eq && rank < take)) atomicOr(&s_bits[ix >> 5], 1u << (ix & 31u));
+    taken += tot;
   }
   __syncthreads();
-  // exclusive scan of the KPT*16 (row, wave) counts in index order; thread t holds entries
-  // t*CPT .. t*CPT+CPT-1
-  constexpr int NE = KPT * kTopkWaves;
-  constexpr int CPT = (NE + kTopkBlock - 1) / kTopkBlock;
-  unsigned cg[CPT], ce[CPT], sg = 0, se = 0;
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int e = tid * CPT + c;
-    cg[c] = e < NE ? (&s_cnt[0][0][0])[e] : 0u;
-    ce[c] = e < NE ? (&s_cnt[1][0][0])[e] : 0u;
-    sg += cg[c];
-    se += ce[c];
-  }
-  unsigned bg, be, tg, te;
-  block_scan2(sg, se, &bg, &be, &tg, &te, s_scan);
-#pragma unroll
-  for (int c = 0; c < CPT; ++c) {
-    const int e = tid * CPT + c;
-    if (e < NE) { (&s_cnt[0][0][0])[e] = bg; (&s_cnt[1][0][0])[e] = be; }
-    bg += cg[c];
-    be += ce[c];
-  }
-  __syncthreads();
-  // tau and krem re-read after the barrier: the per-row comparisons of the counting loop
-  // are then recomputed here instead of being kept alive (96 masks would spill)
-  const unsigned tau2 = s_tk[0], krem2 = s_tk[1];
-  const int zero = (int)s_tk[2];  // element indices are recomputed from it, not kept from the load loop
-#pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int i = zero + tid + j * kTopkBlock;
-    const bool gt = key[j] > tau2;
-    const bool eq = key[j] == tau2;
-    const unsigned long long gm = __ballot(gt);
-    const unsigned long long em = __ballot(eq);
-    const unsigned gb = s_cnt[0][j][w] + (unsigned)__popcll(gm & below);
-    const unsigned eb = s_cnt[1][j][w] + (unsigned)__popcll(em & below);
-    if (gt || (eq && eb < krem2)) {
-      const unsigned pos = gb + min(eb, krem2);
-      if (pos < (unsigned)k) out[pos] = i;   // always true for a correct selection
+  // bitmap -> ascending list: thread t owns words 2t and 2t+1
+  const int w0 = 2 * tid;
+  const unsigned m0 = w0 < nwords ? s_bits[w0] : 0u;
+  const unsigned m1 = w0 + 1 < nwords ? s_bits[w0 + 1] : 0u;
+  unsigned tot;
+  unsigned pos = block_scan((unsigned)__popc(m0) + (unsigned)__popc(m1), &tot, s_scan);
+  static_assert(2 * kTkBlock >= kTopkMaxChunks * (kTopkChunk / 32), "two bitmap words per thread");
+  unsigned m = m0;
+  for (int h = 0; h < 2; ++h) {
+    const int base = (w0 + h) * 32;
+    while (m != 0u) {
+      const int bit = __builtin_ctz(m);
+      m &= m - 1u;
+      if (pos < (unsigned)k) out[pos] = base + bit;   // always true for a correct selection
+      ++pos;
     }
-    __builtin_amdgcn_sched_barrier(0);
+    m = m1;
   }
 }
 
-template <int KPT>
-static void launch_one(const TopkArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL((topk_kernel<KPT>), dim3(B, a.nprob), dim3(kTopkBlock), 0, s, a);
+size_t topk_ws_bytes(int B, int n) {
+  const size_t nch = (size_t)((n + kTopkChunk - 1) / kTopkChunk);
+  const size_t per_row = nch * kTkBins        // part
+                       + nch * (kTopkChunk / 32)   // bits
+                       + 2 * nch * kTopkChunk      // ckey, cidx
+                       + nch                       // ccnt
+                       + 4;                        // sel
+  return (size_t)B * per_row * sizeof(unsigned) + 6 * 256;
+}
+
+TopkWs topk_ws_carve(void* base, int B, int n) {
+  const size_t nch = (size_t)((n + kTopkChunk - 1) / kTopkChunk);
+  char* p = static_cast<char*>(base);
+  auto take = [&](size_t words) {
+    unsigned* r = reinterpret_cast<unsigned*>(p);
+    p += ((words * sizeof(unsigned)) + 255u) & ~size_t(255u);
+    return r;
+  };
+  TopkWs w{};
+  w.part = take((size_t)B * nch * kTkBins);
+  w.bits = take((size_t)B * nch * (kTopkChunk / 32));
+  w.ckey = take((size_t)B * nch * kTopkChunk);
+  w.cidx = take((size_t)B * nch * kTopkChunk);
+  w.ccnt = take((size_t)B * nch);
+  w.sel = take((size_t)B * 4);
+  return w;
 }
 
 hipError_t launch_topk(const TopkArgs& a, int B, hipStream_t s) {
   int nmax = 0;
-  for (int i = 0; i < a.nprob; ++i) nmax = max(nmax, a.p[i].n);
-  if (nmax > 65536) return hipErrorInvalidValue;
-  if (nmax <= 1024) launch_one<1>(a, B, s);
-  else if (nmax <= 4096) launch_one<4>(a, B, s);
-  else if (nmax <= 16384) launch_one<16>(a, B, s);
-  else if (nmax <= 49152) launch_one<48>(a, B, s);
-  else launch_one<64>(a, B, s);
+  for (int i = 0; i < a.nprob; ++i) {
+    if (a.p[i].n > kTopkMaxChunks * kTopkChunk) return hipErrorInvalidValue;
+    nmax = max(nmax, a.p[i].n);
+  }
+  const int nch = (nmax + kTopkChunk - 1) / kTopkChunk;
+  const dim3 grid(nch, B, a.nprob);
+  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kTkBlock), 0, s, a);
+  hipLaunchKernelGGL(topk_classify_kernel, grid, dim3(kTkBlock), 0, s, a);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(B, 1, a.nprob), dim3(kTkBlock), 0, s, a);
   return hipGetLastError();
 }
 

@@ -97,7 +97,7 @@ dv_status dv_predict(const dv_dims* dims, const dv_predictor* pred, const float*
 /* Exact top-k per row (same section; indices sorted as the guide's predictor returns them).
  *   scores [B][n] fp32 -> idx [B][k] int32, ascending. The k largest scores win; equal
  *   scores go to the lower index; -0.0 == +0.0; NaN ranks below -inf. 0 <= k <= n <= 65536.
- *   Uses no workspace (ws may be NULL). */
+ *   Workspace: dv_topk_workspace_bytes(B, n) bytes (may be NULL when k == 0). */
 dv_status dv_topk(const float* scores, int32_t B, int32_t n, int32_t k, int32_t* idx, void* ws,
                   size_t ws_bytes, hipStream_t stream);
 
@@ -151,13 +151,15 @@ dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const 
 
 /* Workspace bytes for every single-layer call above at this shape (the maximum). */
 size_t dv_workspace_bytes(const dv_dims* dims, int32_t B, int32_t k, int32_t kh);
+/* Workspace of dv_topk for B rows of n scores (0 if B or n is out of range). */
+size_t dv_topk_workspace_bytes(int32_t B, int32_t n);
 /* Workspace bytes for dv_lookahead_stack. */
 size_t dv_stack_workspace_bytes(const dv_dims* dims, int32_t B, int32_t k, int32_t kh);
 
 /* Observability: time the head-sparse q/k/v projection launch (the step's largest gather).
  * dv_timing_start(n) creates n event pairs and returns n (-1 if already active or n <= 0);
- * while active, each q/k/v launch of any call records the next pair on its own stream
- * until n are used. dv_timing_stop(ms, n) waits for the recorded pairs, writes the
+ * while active, each q/k/v launch of any call takes the next pair as the begin/end
+ * timestamps of its own dispatch (hipExtLaunchKernel start/stop events) until n are used. dv_timing_stop(ms, n) waits for the recorded pairs, writes the
  * duration of each in milliseconds to ms[0..] (at most n; ms may be NULL), destroys the
  * events and returns the number recorded (-1 on a HIP error or if not active). */
 int32_t dv_timing_start(int32_t n);

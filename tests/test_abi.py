@@ -118,6 +118,18 @@ def test_validation_codes_topk():
     assert f(None, 1, 100, 5, FAKE, None, 0, None) == 1
     assert f(FAKE, 0, 100, 5, FAKE, None, 0, None) == 2
     assert f(FAKE, 1, 100, 0, None, None, 0, None) == 0       # k = 0: nothing to do, nothing launched
+    need = _lib.lib().dv_topk_workspace_bytes(1, 100)
+    assert need > 0 and need % 256 == 0
+    assert f(FAKE, 1, 100, 5, FAKE, None, 0, None) == 7       # k > 0 needs the workspace
+    assert f(FAKE, 1, 100, 5, FAKE, FAKE, need - 1, None) == 7
+
+
+def test_topk_workspace_size():
+    g = _lib.lib().dv_topk_workspace_bytes
+    assert g(0, 100) == 0 and g(1, 0) == 0 and g(1, 65537) == 0
+    one, two = g(1, 49152), g(2, 49152)
+    # per row at least: 12 chunk histograms of 2048 counts, the candidate keys and positions
+    assert one >= 4 * (12 * 2048 + 2 * 49152) and two >= 2 * one - 2048
 
 
 def test_python_raises_with_status_name():
