@@ -3,6 +3,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
@@ -127,6 +128,9 @@ dv_status check_pred(const dv_predictor* P) {
 // ---------------------------------------------------------------------------
 struct Layout {
   size_t z, s_mlp, s_head, idx, heads, qkv, apart, o, h1, u, part, tk_mlp, tk_head, total;
+  // batched path (B >= 2): union bitmaps and lists, fp16 operands
+  size_t ubits, hbits, ulist, uhlist, counts, xh, xl, zh, zl, cu, co;
+  int max_u, max_uh;
   int max_chunks;
 };
 
@@ -152,6 +156,22 @@ Layout layout_of(const dv_dims* d, int B, int k, int kh) {
   L.part = take(f * Bz * dv::rowaxpy_max_rg() * d->d_model);
   L.tk_mlp = take(dv::topk_ws_bytes(B, d->d_ffn));
   L.tk_head = take(dv::topk_ws_bytes(B, d->n_heads));
+  if (B >= 2) {
+    const size_t fw = (size_t)(d->d_ffn + 31) / 32, hw = (size_t)(d->n_heads + 31) / 32;
+    L.max_u = (int)std::min<long long>(d->d_ffn, (long long)B * k);
+    L.max_uh = (int)std::min<long long>(d->n_heads, (long long)B * kh);
+    L.ubits = take(4 * (Bz + 1) * fw);
+    L.hbits = take(4 * (Bz + 1) * hw);
+    L.ulist = take(4 * (size_t)d->d_ffn);
+    L.uhlist = take(4 * (size_t)d->n_heads);
+    L.counts = take(4 * 4);
+    L.xh = take(2 * Bz * d->d_model);
+    L.xl = take(2 * Bz * d->d_model);
+    L.zh = take(2 * Bz * (d->rank_mlp + d->rank_head));
+    L.zl = take(2 * Bz * (d->rank_mlp + d->rank_head));
+    L.cu = take(2 * Bz * (size_t)L.max_u);
+    L.co = take(2 * Bz * (size_t)L.max_uh * d->head_dim);
+  }
   L.total = off;
   return L;
 }
@@ -220,8 +240,48 @@ void predict_stage1_segs(const dv_dims* d, const dv_predictor* P, const float* x
 dv_status run_predict_stage2(const dv_dims* d, const dv_predictor* P, int B, float* s_mlp, float* s_head,
                              const float* z, int cus, hipStream_t st);
 
+// The batched path (union of the rows' selections on the matrix cores) serves fp16 weights
+// and 2..32 rows; other batches run every row through the single-row kernels.
+bool batched(const dv_dims* d, int B) { return B >= 2 && B <= dv::kBatchMax && is_f16(d); }
+
+dv::GemmRowsArgs rows_args(const void* W, long long ld, int dlen, const int32_t* sel, const int* nsel, int G,
+                           int n_groups, int B, const _Float16* X, long long ldx) {
+  dv::GemmRowsArgs g{};
+  g.W = W; g.ld = ld; g.d = dlen; g.sel = sel; g.n_groups_sel = nsel; g.G = G; g.n_groups = n_groups; g.B = B;
+  g.X = X; g.ldx = ldx;
+  return g;
+}
+
+// Batched predictor: both factors as dense MFMA products over all B rows. The activations
+// (x, then z) enter as fp16 high parts plus fp16 remainders, so the scores keep fp32-like
+// precision (the fp16 weights are exact).
+dv_status run_predict_batched(const dv_dims* d, const dv_predictor* P, const float* x, int B, float* s_mlp,
+                              float* s_head, const Layout& L, void* ws, hipStream_t st) {
+  const int rm = d->rank_mlp, rh = d->rank_head, D = d->d_model;
+  _Float16* xh = at<_Float16>(ws, L.xh);
+  _Float16* xl = at<_Float16>(ws, L.xl);
+  _Float16* zh = at<_Float16>(ws, L.zh);
+  _Float16* zl = at<_Float16>(ws, L.zl);
+  DV_HIP(dv::launch_rows_norm_f16(x, D, nullptr, D, 0.f, B, xh, xl, D, st));
+  dv::GemmRowsArgs a = rows_args(P->p1_mlp, D, D, nullptr, nullptr, 1, rm, B, xh, D);
+  a.X_lo = xl; a.mode = dv::kGemmOutF16; a.outh = zh; a.outh_lo = zl; a.ldo = rm + rh;
+  DV_HIP(dv::launch_gemm_rows(a, rm, st));
+  a = rows_args(P->p1_head, D, D, nullptr, nullptr, 1, rh, B, xh, D);
+  a.X_lo = xl; a.mode = dv::kGemmOutF16; a.outh = zh + rm; a.outh_lo = zl + rm; a.ldo = rm + rh;
+  DV_HIP(dv::launch_gemm_rows(a, rh, st));
+  a = rows_args(P->p2_mlp, rm, rm, nullptr, nullptr, 1, d->d_ffn, B, zh, rm + rh);
+  a.X_lo = zl; a.mode = dv::kGemmOutF32; a.outf = s_mlp; a.ldo = d->d_ffn;
+  DV_HIP(dv::launch_gemm_rows(a, d->d_ffn, st));
+  a = rows_args(P->p2_head, rh, rh, nullptr, nullptr, 1, d->n_heads, B, zh + rm, rm + rh);
+  a.X_lo = zl + rm; a.mode = dv::kGemmOutF32; a.outf = s_head; a.ldo = d->n_heads;
+  DV_HIP(dv::launch_gemm_rows(a, d->n_heads, st));
+  return DV_OK;
+}
+
 dv_status run_predict(const dv_dims* d, const dv_predictor* P, const float* x, int B, float* s_mlp,
-                      float* s_head, float* z, int cus, hipStream_t st) {
+                      float* s_head, const Layout& L, void* ws, int cus, hipStream_t st) {
+  if (batched(d, B)) return run_predict_batched(d, P, x, B, s_mlp, s_head, L, ws, st);
+  float* z = at<float>(ws, L.z);
   const bool f16 = is_f16(d);
   dv::RowDotArgs a{};
   a.nseg = 2; a.d = d->d_model; a.eps = 0.f;
@@ -325,11 +385,114 @@ dv_status run_mlp(const dv_dims* d, const dv_layer* Lw, const float* x, const fl
   return DV_OK;
 }
 
+// Union of the rows' neuron sets (problem 0) and/or head sets (problem 1).
+dv_status run_union(const dv_dims* d, int B, const int32_t* idx, int k, const int32_t* heads, int kh, const Layout& L,
+                    void* ws, hipStream_t st) {
+  dv::UnionArgs u{};
+  u.B = B;
+  int* counts = at<int>(ws, L.counts);
+  if (idx != nullptr) u.p[u.nprob++] = {idx, k, d->d_ffn, k, at<unsigned>(ws, L.ubits), at<int32_t>(ws, L.ulist), counts};
+  if (heads != nullptr)
+    u.p[u.nprob++] = {heads, kh, d->n_heads, kh, at<unsigned>(ws, L.hbits), at<int32_t>(ws, L.uhlist), counts + 1};
+  if (u.nprob == 0) return DV_OK;
+  if (u.nprob == 1) u.p[1] = u.p[0];
+  DV_HIP(dv::launch_union(u, st));
+  return DV_OK;
+}
+
+// Batched head-sparse attention: q/k/v over the union of the rows' heads (MFMA), decode
+// attention per (row, selected head), output projection over the union (MFMA) + reduce.
+dv_status run_attn_batched(const dv_dims* d, const dv_layer* Lw, const float* x, const float* norm_g, int B,
+                           const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* y, const float* resid,
+                           const Layout& L, void* ws, int cus, hipStream_t st, hipEvent_t ev_after_qkv, bool union_done) {
+  const int D = d->d_model, dh = d->head_dim, H = d->n_heads;
+  const int hw = (H + 31) / 32;
+  const int* counts = at<int>(ws, L.counts);
+  float* qkv = at<float>(ws, L.qkv);
+  float* o = at<float>(ws, L.o);
+  if (kh > 0) {
+    if (!union_done) DV_TRY(run_union(d, B, nullptr, 0, heads, kh, L, ws, st));
+    _Float16* xh = at<_Float16>(ws, L.xh);
+    DV_HIP(dv::launch_rows_norm_f16(x, D, norm_g, D, 1e-5f, B, xh, nullptr, D, st));
+    dv::GemmRowsArgs q = rows_args(Lw->wqkv, D, D, at<int32_t>(ws, L.uhlist), counts + 1, 3 * dh, H, B, xh, D);
+    q.bias = Lw->bqkv; q.rowbits = at<unsigned>(ws, L.hbits); q.bits_words = hw;
+    q.mode = dv::kGemmOutQkv; q.outf = qkv; q.kh = kh;
+    DV_HIP(dv::launch_gemm_rows(q, L.max_uh * 3 * dh, st));
+  }
+  if (ev_after_qkv) DV_HIP(hipEventRecord(ev_after_qkv, st));
+  if (kh > 0) {
+    dv::AttnArgs at_{};
+    at_.qkv = qkv; at_.heads = heads; at_.kh = kh; at_.n_heads = H; at_.dh = dh; at_.t_past = t_past;
+    at_.t_max = d->t_max; at_.k_cache = kc; at_.v_cache = vc; at_.partial = at<float>(ws, L.apart);
+    at_.o = o;
+    if (!dv::attn_plan(dh, true, t_past + 1, kh, B, cus, &at_.chunk, &at_.n_chunks))
+      return fail(DV_ERR_DIMS, "head_dim unsupported");
+    if (at_.n_chunks > L.max_chunks) return fail(DV_ERR_DIMS, "internal: attention chunk plan");
+    DV_HIP(dv::launch_attn(at_, true, B, st));
+    _Float16* co = at<_Float16>(ws, L.co);
+    const long long ldc = (long long)L.max_uh * dh;
+    DV_HIP(dv::launch_heads_to_union(o, kh, dh, at<int32_t>(ws, L.uhlist), counts + 1, at<unsigned>(ws, L.hbits), hw,
+                                     B, L.max_uh, co, ldc, st));
+  }
+  dv::GemmColsArgs c{};
+  c.W = Lw->wo; c.ld = D; c.d = D; c.sel = at<int32_t>(ws, L.uhlist); c.n_groups_sel = counts + 1; c.G = dh;
+  c.n_groups = H; c.B = B; c.C = at<_Float16>(ws, L.co); c.ldc = (long long)L.max_uh * dh;
+  c.partial = at<float>(ws, L.part); c.RG = dv::gemm_cols_rg(D, std::max(1, L.max_uh * dh), B, cus);
+  dv::RowAxpyArgs r{};
+  r.d = D; r.partial = c.partial; r.RG = c.RG; r.bias = Lw->bo; r.resid = resid; r.ldr = D; r.out = y; r.ldo = D;
+  if (kh > 0) {
+    DV_HIP(dv::launch_gemm_cols(c, st));
+  } else {
+    r.partial = nullptr;   // no heads: bias + residual only
+    r.RG = 1;
+  }
+  DV_HIP(dv::launch_axpy_reduce(r, B, st));
+  return DV_OK;
+}
+
+// Batched sparse MLP: up-projection over the union of the rows' neurons with per-row ReLU
+// outputs (zero where a row does not select the neuron), down-projection over the union.
+dv_status run_mlp_batched(const dv_dims* d, const dv_layer* Lw, const float* x, const float* norm_g, int B,
+                          const int32_t* idx, int k, float* y, const float* resid, const Layout& L, void* ws, int cus,
+                          hipStream_t st, bool union_done) {
+  const int D = d->d_model, F = d->d_ffn;
+  const int* counts = at<int>(ws, L.counts);
+  dv::RowAxpyArgs r{};
+  r.d = D; r.partial = at<float>(ws, L.part); r.bias = Lw->b2; r.resid = resid; r.ldr = D; r.out = y; r.ldo = D;
+  if (k == 0) {   // no neurons: bias + residual only
+    r.partial = nullptr;
+    r.RG = 1;
+    DV_HIP(dv::launch_axpy_reduce(r, B, st));
+    return DV_OK;
+  }
+  if (!union_done) DV_TRY(run_union(d, B, idx, k, nullptr, 0, L, ws, st));
+  _Float16* xh = at<_Float16>(ws, L.xh);
+  DV_HIP(dv::launch_rows_norm_f16(x, D, norm_g, D, 1e-5f, B, xh, nullptr, D, st));
+  _Float16* cu = at<_Float16>(ws, L.cu);
+  dv::GemmRowsArgs a = rows_args(Lw->w1t, D, D, at<int32_t>(ws, L.ulist), counts, 1, F, B, xh, D);
+  a.bias = Lw->b1; a.relu = 1; a.rowbits = at<unsigned>(ws, L.ubits); a.bits_words = (F + 31) / 32;
+  a.mode = dv::kGemmOutF16; a.outh = cu; a.ldo = L.max_u;
+  DV_HIP(dv::launch_gemm_rows(a, L.max_u, st));
+  dv::GemmColsArgs c{};
+  c.W = Lw->w2; c.ld = D; c.d = D; c.sel = at<int32_t>(ws, L.ulist); c.n_groups_sel = counts; c.G = 1; c.n_groups = F;
+  c.B = B; c.C = cu; c.ldc = L.max_u; c.partial = r.partial; c.RG = dv::gemm_cols_rg(D, L.max_u, B, cus);
+  r.RG = c.RG;
+  DV_HIP(dv::launch_gemm_cols(c, st));
+  DV_HIP(dv::launch_axpy_reduce(r, B, st));
+  return DV_OK;
+}
+
 dv_status run_layer(const dv_dims* d, const dv_layer* Lw, const float* x, int B, const int32_t* idx, int k,
                     const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* x_out,
                     const Layout& L, void* ws, int cus, hipStream_t st, hipEvent_t ev_after_qkv = nullptr,
                     const dv::RowDotSeg* extra = nullptr, int n_extra = 0) {
   float* h1 = at<float>(ws, L.h1);
+  if (batched(d, B)) {
+    if (n_extra != 0) return fail(DV_ERR_DIMS, "internal: fused segments on the batched path");
+    DV_TRY(run_union(d, B, k > 0 ? idx : nullptr, k, kh > 0 ? heads : nullptr, kh, L, ws, st));
+    DV_TRY(run_attn_batched(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, t_past, h1, x, L, ws, cus, st, ev_after_qkv, true));
+    return run_mlp_batched(d, Lw, h1, Lw->g2, B, idx, k, x_out, h1, L, ws, cus, st, true);
+  }
   DV_TRY(run_attn(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, t_past, h1, x, L, ws, cus, st, ev_after_qkv, extra,
                   n_extra));
   DV_TRY(run_mlp(d, Lw, h1, Lw->g2, B, idx, k, x_out, h1, L, ws, cus, st));
@@ -446,7 +609,7 @@ dv_status dv_predict(const dv_dims* dims, const dv_predictor* pred, const float*
   DV_TRY(check_ws(ws, ws_bytes, L.total));
   DeviceInfo* di;
   DV_TRY(device_info(&di, false));
-  return run_predict(dims, pred, x_pred, B, s_mlp, s_head, at<float>(ws, L.z), di->cus, stream);
+  return run_predict(dims, pred, x_pred, B, s_mlp, s_head, L, ws, di->cus, stream);
 }
 
 size_t dv_topk_workspace_bytes(int32_t B, int32_t n) {
@@ -483,6 +646,7 @@ dv_status dv_sparse_mlp(const dv_dims* dims, const dv_layer* layer, const float*
   DV_TRY(check_ws(ws, ws_bytes, L.total));
   DeviceInfo* di;
   DV_TRY(device_info(&di, false));
+  if (batched(dims, B)) return run_mlp_batched(dims, layer, xn, nullptr, B, idx, k, y, nullptr, L, ws, di->cus, stream, false);
   return run_mlp(dims, layer, xn, nullptr, B, idx, k, y, nullptr, L, ws, di->cus, stream);
 }
 
@@ -500,6 +664,9 @@ dv_status dv_sparse_attn(const dv_dims* dims, const dv_layer* layer, const float
   DV_TRY(check_ws(ws, ws_bytes, L.total));
   DeviceInfo* di;
   DV_TRY(device_info(&di, false));
+  if (batched(dims, B))
+    return run_attn_batched(dims, layer, xn, nullptr, B, heads, kh, k_cache, v_cache, t_past, y, nullptr, L, ws,
+                            di->cus, stream, nullptr, false);
   return run_attn(dims, layer, xn, nullptr, B, heads, kh, k_cache, v_cache, t_past, y, nullptr, L, ws,
                   di->cus, stream);
 }
@@ -530,8 +697,8 @@ dv_status dv_layer_step(const dv_dims* dims, const dv_layer* layer, const dv_pre
   if (inline_pred) {
     int32_t* io = idx_out ? idx_out : at<int32_t>(ws, L.idx);
     int32_t* ho = heads_out ? heads_out : at<int32_t>(ws, L.heads);
-    DV_TRY(run_predict(dims, pred, x_pred, B, at<float>(ws, L.s_mlp), at<float>(ws, L.s_head),
-                       at<float>(ws, L.z), di->cus, stream));
+    DV_TRY(run_predict(dims, pred, x_pred, B, at<float>(ws, L.s_mlp), at<float>(ws, L.s_head), L, ws, di->cus,
+                       stream));
     DV_TRY(run_topk2(at<float>(ws, L.s_mlp), dims->d_ffn, k, io, at<float>(ws, L.s_head), dims->n_heads, kh,
                      ho, B, at<char>(ws, L.tk_mlp), at<char>(ws, L.tk_head), stream));
     idx = io;
@@ -605,8 +772,8 @@ dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const 
   hipStream_t st_side = two ? side_stream : stream;
   if (h_all) DV_HIP(hipMemcpyAsync(h_all, x, vecb, hipMemcpyDeviceToDevice, stream));
   // Layer 0's sets come from the stack input, before any layer runs.
-  DV_TRY(run_predict(dims, &preds[0], h_in(0), B, at<float>(ws, L.s_mlp), at<float>(ws, L.s_head),
-                     at<float>(ws, L.z), cus, stream));
+  DV_TRY(run_predict(dims, &preds[0], h_in(0), B, at<float>(ws, L.s_mlp), at<float>(ws, L.s_head), L, ws, cus,
+                     stream));
   DV_TRY(topk_sets(0, ws, stream));
   for (int l = 0; l < n_layers; ++l) {
     if (two && l >= 1) DV_HIP(hipStreamWaitEvent(stream, di->ev_sel[l % 2], 0));
@@ -614,15 +781,20 @@ dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const 
     // the same vector as layer l's q/k/v projection and rides in that launch; stage 2 and the
     // top-k then run on the side stream while layer l finishes.
     const bool ahead = l + 1 < n_layers;
+    const bool fuse = ahead && !batched(dims, B);
     dv::RowDotSeg p1[2];
-    if (ahead) predict_stage1_segs(dims, &preds[l + 1], h_in(l), at<float>(ws_side, L.z), p1);
+    if (fuse) predict_stage1_segs(dims, &preds[l + 1], h_in(l), at<float>(ws_side, L.z), p1);
     DV_TRY(run_layer(dims, &layers[l], h_in(l), B, sel_idx(l), k, sel_heads(l), kh, k_caches[l], v_caches[l],
                      t_past, h_outp(l), L, ws, cus, stream, (ahead && two) ? di->ev_in : nullptr,
-                     ahead ? p1 : nullptr, ahead ? 2 : 0));
+                     fuse ? p1 : nullptr, fuse ? 2 : 0));
     if (ahead) {
       if (two) DV_HIP(hipStreamWaitEvent(st_side, di->ev_in, 0));
-      DV_TRY(run_predict_stage2(dims, &preds[l + 1], B, at<float>(ws_side, L.s_mlp), at<float>(ws_side, L.s_head),
-                                at<float>(ws_side, L.z), cus, st_side));
+      if (fuse)
+        DV_TRY(run_predict_stage2(dims, &preds[l + 1], B, at<float>(ws_side, L.s_mlp), at<float>(ws_side, L.s_head),
+                                  at<float>(ws_side, L.z), cus, st_side));
+      else
+        DV_TRY(run_predict(dims, &preds[l + 1], h_in(l), B, at<float>(ws_side, L.s_mlp), at<float>(ws_side, L.s_head),
+                           L, ws_side, cus, st_side));
       DV_TRY(topk_sets(l + 1, ws_side, st_side));
       if (two) DV_HIP(hipEventRecord(di->ev_sel[(l + 1) % 2], st_side));
     }

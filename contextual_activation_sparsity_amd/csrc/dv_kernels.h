@@ -126,4 +126,77 @@ size_t topk_ws_bytes(int B, int n);              // scratch of one problem
 TopkWs topk_ws_carve(void* base, int B, int n);  // base: 256-byte aligned, topk_ws_bytes long
 hipError_t launch_topk(const TopkArgs& a, int B, hipStream_t s);
 
+// ---------------------------------------------------------------------------
+// Batched decode on the union of the rows' selections (k_batched.hip).
+// ---------------------------------------------------------------------------
+constexpr int kUnionMaxN = 65536;    // groups (neurons or heads) per problem
+constexpr int kBatchMax = 32;        // rows per batched launch
+constexpr int kBatchMaxRG = 16;      // row groups of the down-projection
+struct UnionProb {
+  const int32_t* idx;       // [B][idx_bstride]: the row's k selected groups (ascending)
+  long long idx_bstride;
+  int n;                    // groups
+  int k;                    // selected per row
+  unsigned* bits;           // [B + 1][ceil(n/32)]: row bitmaps, then their OR
+  int32_t* list;            // [n]: the OR as an ascending list
+  int* count;               // its length
+};
+struct UnionArgs {
+  UnionProb p[2];
+  int nprob;
+  int B;
+};
+hipError_t launch_union(const UnionArgs& a, hipStream_t s);
+hipError_t launch_rows_norm_f16(const float* x, long long ldx, const float* g, int d, float eps, int B, _Float16* out,
+                                _Float16* out_lo, long long ldo, hipStream_t s);
+
+constexpr int kGemmOutF16 = 0;       // outh[b][i], fp16, 0 where the row does not select the group
+constexpr int kGemmOutQkv = 1;       // outf[b][slot][G], only groups the row selects (slot = rank)
+constexpr int kGemmOutF32 = 2;       // outf[b][i], fp32, 0 where the row does not select the group
+struct GemmRowsArgs {                // out[b][i] = act(W[row_i] . X[b] + bias[row_i]), MFMA
+  const void* W;                     // fp16 rows [n_groups * G][ld]
+  long long ld;
+  int d;                             // row length (multiple of 8)
+  const int32_t* sel;                // selected groups (ascending; nullable = all)
+  const int* n_groups_sel;           // device count of sel (nullable = n_groups)
+  int G;
+  int n_groups;
+  int B;
+  const _Float16* X;                 // [B][ldx]
+  const _Float16* X_lo;              // nullable: rounding remainders of X (same layout)
+  long long ldx;
+  const float* bias;                 // nullable
+  int relu;
+  const unsigned* rowbits;           // [B][bits_words] (nullable = every row selects every group)
+  int bits_words;
+  int mode;
+  _Float16* outh;
+  _Float16* outh_lo;                 // nullable: remainders of outh (kGemmOutF16)
+  float* outf;
+  long long ldo;
+  int kh;                            // slots per row (kGemmOutQkv)
+};
+hipError_t launch_gemm_rows(const GemmRowsArgs& a, int max_rows, hipStream_t s);
+
+struct GemmColsArgs {                // partial[b][rg][c] = sum_k C[b][k] W[row_k][c], MFMA
+  const void* W;                     // fp16 rows [n_groups * G][ld]
+  long long ld;
+  int d;                             // output columns (multiple of 8)
+  const int32_t* sel;
+  const int* n_groups_sel;
+  int G;
+  int n_groups;
+  int B;
+  const _Float16* C;                 // [B][ldc] coefficients in the union's row order
+  long long ldc;
+  float* partial;                    // [B][RG][d]
+  int RG;
+};
+int gemm_cols_rg(int d, int max_rows, int B, int cus);
+hipError_t launch_gemm_cols(const GemmColsArgs& a, hipStream_t s);
+hipError_t launch_heads_to_union(const float* o, int kh, int dh, const int32_t* uh, const int* n_uh, const unsigned* hbits,
+                                 int hwords, int B, int max_uh, _Float16* C, long long ldc, hipStream_t s);
+// out[b][c] = sum_rg partial[b][rg][c] (group order) + bias[c] + resid[b][c]
+hipError_t launch_axpy_reduce(const RowAxpyArgs& a, int B, hipStream_t s);
+
 }  // namespace dv

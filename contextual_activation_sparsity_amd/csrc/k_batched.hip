@@ -1,0 +1,421 @@
+// Batched decode (B >= 2 rows per step) on the union of the rows' selections.
+//
+// Each row keeps its own selection (the step is per-row masked, DejaVu Guide, "Head-Pruned
+// Attention Dispatch" and the sparse MLP of "Step-by-Step Implementation", applied row by
+// row); the union only shares the weight traffic: every selected weight row is read once
+// and multiplied against all B activation rows on the matrix cores.
+//
+//  * union_zero / union_scatter / union_list: per-row bitmaps of the selected groups (neurons
+//    or heads), their OR, and the OR as an ascending list with its length in device memory.
+//  * rows_norm_f16: RMSNorm of each row, rounded to fp16 (the MFMA operand type).
+//  * gemm_rows (up-projection, q/k/v and W1; both predictor factors): out[b][i] =
+//    act(W[row_i] . X[b] + bias), masked per row. A wave owns 16 gathered rows; A fragments
+//    are 16-byte loads along a weight row, B fragments 16-byte loads along an activation
+//    row, fp32 accumulation with v_mfma_f32_16x16x32_f16. With a low part X_lo the product
+//    is taken twice (W . X_hi + W . X_lo): the fp16 weights are exact, so the result then
+//    carries fp32-like activation precision (used for the predictor's scores).
+//  * gemm_cols (down-projection, Wo and W2): partial[b][rg][c] = sum over the rows of row
+//    group rg of C[b][k] * W[row_k][c]. The weight tile (32 rows x 128 columns) is staged
+//    in LDS transposed so each lane's B fragment (8 consecutive k at one column) is one
+//    16-byte LDS read. The row groups are summed by the ordered reduce kernel of the
+//    gather-axpy.
+// Every sum has a fixed order: results are bitwise reproducible.
+#include <algorithm>
+
+#include "dv_device.h"
+#include "dv_kernels.h"
+
+namespace dv {
+
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bool bit_of(const unsigned* bits, int j) { return (bits[j >> 5] >> (j & 31)) & 1u; }
+
+// Number of set bits of `bits` below position j (the rank of j in an ascending list).
+__device__ __forceinline__ int rank_below(const unsigned* bits, int j) {
+  int r = 0;
+  for (int w = 0; w < (j >> 5); ++w) r += __popc(bits[w]);
+  return r + __popc(bits[j >> 5] & ((1u << (j & 31)) - 1u));
+}
+
+// ---------------------------------------------------------------------------
+// union of the rows' selections
+// ---------------------------------------------------------------------------
+__global__ void union_zero_kernel(UnionArgs a) {
+  const UnionProb& P = blockIdx.y == 0 ? a.p[0] : a.p[1];
+  const int words = (P.n + 31) / 32;
+  const int total = (a.B + 1) * words;   // B row bitmaps + the union
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) P.bits[i] = 0u;
+}
+
+__global__ void union_scatter_kernel(UnionArgs a) {
+  const UnionProb& P = blockIdx.y == 0 ? a.p[0] : a.p[1];
+  const int words = (P.n + 31) / 32;
+  const long long total = (long long)a.B * P.k;
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < total; e += (long long)gridDim.x * blockDim.x) {
+    const int b = (int)(e / P.k);
+    const int j = P.idx[(long long)b * P.idx_bstride + (e - (long long)b * P.k)];
+    if ((unsigned)j >= (unsigned)P.n) continue;   // out-of-range entries select nothing
+    const unsigned m = 1u << (j & 31);
+    atomicOr(&P.bits[(long long)b * words + (j >> 5)], m);
+    atomicOr(&P.bits[(long long)a.B * words + (j >> 5)], m);
+  }
+}
+
+constexpr int kUnionBlock = 1024;
+// One block per problem: union bitmap -> ascending list + its length.
+__global__ __launch_bounds__(kUnionBlock) void union_list_kernel(UnionArgs a) {
+  __shared__ unsigned s_scan[kUnionBlock / kWave];
+  const UnionProb& P = blockIdx.x == 0 ? a.p[0] : a.p[1];
+  const int words = (P.n + 31) / 32;
+  const unsigned* ub = P.bits + (long long)a.B * words;
+  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+  constexpr int WPT = kUnionMaxN / 32 / kUnionBlock;   // words per thread
+  unsigned m[WPT];
+  unsigned cnt = 0;
+#pragma unroll
+  for (int q = 0; q < WPT; ++q) {
+    const int wi = tid * WPT + q;
+    m[q] = wi < words ? ub[wi] : 0u;
+    cnt += __popc(m[q]);
+  }
+  unsigned incl = cnt;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const unsigned t = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += t;
+  }
+  if (lane == kWave - 1) s_scan[w] = incl;
+  __syncthreads();
+  unsigned before = 0, total = 0;
+  for (int i = 0; i < kUnionBlock / kWave; ++i) {
+    if (i < w) before += s_scan[i];
+    total += s_scan[i];
+  }
+  unsigned pos = before + incl - cnt;
+#pragma unroll
+  for (int q = 0; q < WPT; ++q) {
+    unsigned mm = m[q];
+    const int base = (tid * WPT + q) * 32;
+    while (mm != 0u) {
+      const int bit = __builtin_ctz(mm);
+      mm &= mm - 1u;
+      P.list[pos++] = base + bit;
+    }
+  }
+  if (tid == 0) *P.count = (int)total;
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm of each row (or a plain copy when g is null), rounded to fp16; with out_lo the
+// rounding remainder goes there too (v = hi + lo to about 22 bits, for the split products)
+// ---------------------------------------------------------------------------
+constexpr int kNormBlock = 256;
+__global__ __launch_bounds__(kNormBlock) void rows_norm_f16_kernel(const float* x, long long ldx, const float* g, int d,
+                                                                    float eps, _Float16* out, _Float16* out_lo,
+                                                                    long long ldo) {
+  __shared__ float s_red[kNormBlock / kWave];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const float* xb = x + (long long)b * ldx;
+  float ss = 0.f;
+  for (int c = tid * 4; c < d; c += kNormBlock * 4) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(xb + c);
+    ss = fmaf(t[0], t[0], ss); ss = fmaf(t[1], t[1], ss); ss = fmaf(t[2], t[2], ss); ss = fmaf(t[3], t[3], ss);
+  }
+  ss = group_sum<kWave>(ss);
+  if (tid % kWave == 0) s_red[tid / kWave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormBlock / kWave; ++i) tot += s_red[i];
+  const float inv = g ? 1.0f / sqrtf(tot / (float)d + eps) : 1.0f;   // no gain: plain cast
+  _Float16* ob = out + (long long)b * ldo;
+  for (int c = tid * 4; c < d; c += kNormBlock * 4) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(xb + c);
+    const f32x4 gg = g ? *reinterpret_cast<const f32x4*>(g + c) : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = t[e] * inv * gg[e];
+      const _Float16 hi = static_cast<_Float16>(v);
+      ob[c + e] = hi;
+      if (out_lo) out_lo[(long long)b * ldo + c + e] = static_cast<_Float16>(v - static_cast<float>(hi));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gemm_rows: up-projection over gathered rows
+// ---------------------------------------------------------------------------
+constexpr int kGemmBlock = 256;   // 4 waves
+constexpr int kRowsUK = 8;        // K steps (32 each) whose loads are issued together
+
+template <int NT, bool SPLIT>
+__global__ __launch_bounds__(kGemmBlock) void gemm_rows_kernel(GemmRowsArgs a) {
+  const int lane = threadIdx.x % kWave;
+  const int wv = threadIdx.x / kWave;
+  const int nrows = (a.n_groups_sel ? *a.n_groups_sel : a.n_groups) * a.G;
+  const int tile = blockIdx.x * (kGemmBlock / kWave) + wv;
+  const int r0 = tile * 16;
+  if (r0 >= nrows) return;   // whole wave idle (no barriers in this kernel)
+  const int lr = lane % 16, lg = lane / 16;
+  const half_t* W = reinterpret_cast<const half_t*>(a.W);
+  // A operand: weight row of lane row lr
+  const int ia = r0 + lr;
+  long long wrow = -1;
+  if (ia < nrows) {
+    const int g = ia / a.G;
+    const int grp = a.sel ? a.sel[g] : g;
+    if ((unsigned)grp < (unsigned)a.n_groups) wrow = (long long)grp * a.G + (ia - g * a.G);
+  }
+  const half_t* wp = W + (wrow >= 0 ? wrow : 0) * a.ld + 8 * lg;
+  const _Float16* xp[NT];
+  const _Float16* xq[NT];   // low parts (SPLIT)
+  bool xv[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int b = nt * 16 + lr;
+    xv[nt] = b < a.B;
+    xp[nt] = a.X + (long long)(xv[nt] ? b : 0) * a.ldx + 8 * lg;
+    xq[nt] = SPLIT ? a.X_lo + (long long)(xv[nt] ? b : 0) * a.ldx + 8 * lg : nullptr;
+  }
+  f4v acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
+  const int nk = (a.d + 31) / 32;
+  for (int k0 = 0; k0 < nk; k0 += kRowsUK) {
+    u32x4 av[kRowsUK];
+    h8v bv[kRowsUK][NT];
+    h8v bl[SPLIT ? kRowsUK : 1][NT];
+#pragma unroll
+    for (int u = 0; u < kRowsUK; ++u) {
+      const int ks = k0 + u;
+      const bool ok = ks < nk && ks * 32 + 8 * lg + 8 <= a.d;   // d is a multiple of 8
+      av[u] = (ok && wrow >= 0) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + (long long)ks * 32))
+                                : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (ok && xv[nt]) bv[u][nt] = *reinterpret_cast<const h8v*>(xp[nt] + (long long)ks * 32);
+        else bv[u][nt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+        if constexpr (SPLIT) {
+          if (ok && xv[nt]) bl[u][nt] = *reinterpret_cast<const h8v*>(xq[nt] + (long long)ks * 32);
+          else bl[u][nt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRowsUK; ++u) {
+      const h8v ah = __builtin_bit_cast(h8v, av[u]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv[u][nt], acc[nt], 0, 0, 0);
+        if constexpr (SPLIT) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl[u][nt], acc[nt], 0, 0, 0);
+      }
+    }
+  }
+  // D layout: lane holds column (batch row) lr of tile nt, gathered rows r0 + 4*lg + e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = r0 + 4 * lg + e;
+    if (i >= nrows) continue;
+    const int g = i / a.G;
+    const int wi = i - g * a.G;
+    const int grp = a.sel ? a.sel[g] : g;
+    const bool gv = (unsigned)grp < (unsigned)a.n_groups;
+    const long long row = gv ? (long long)grp * a.G + wi : 0;
+    const float bias = (gv && a.bias) ? a.bias[row] : 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int b = nt * 16 + lr;
+      if (b >= a.B) continue;
+      const unsigned* rb = a.rowbits ? a.rowbits + (long long)b * a.bits_words : nullptr;
+      const bool on = gv && (rb == nullptr || bit_of(rb, grp));
+      float v = acc[nt][e] + bias;
+      if (a.relu) v = fmaxf(v, 0.f);
+      if (a.mode == kGemmOutF16) {
+        const float vv = on ? v : 0.f;
+        const _Float16 hi = static_cast<_Float16>(vv);
+        a.outh[(long long)b * a.ldo + i] = hi;
+        if (a.outh_lo) a.outh_lo[(long long)b * a.ldo + i] = static_cast<_Float16>(vv - static_cast<float>(hi));
+      } else if (a.mode == kGemmOutF32) {
+        a.outf[(long long)b * a.ldo + i] = on ? v : 0.f;
+      } else if (on && rb != nullptr) {   // q/k/v into the row's own slot order
+        const int slot = rank_below(rb, grp);
+        a.outf[((long long)b * a.kh + slot) * a.G + wi] = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gemm_cols: down-projection over gathered rows, row groups -> partials
+// ---------------------------------------------------------------------------
+constexpr int kColsNT = 128;        // output columns per block (8 MFMA column tiles)
+constexpr int kColsKT = 32;         // gathered rows per LDS tile
+constexpr int kColsPad = 8;         // halfs of padding per transposed column
+constexpr int kColsLd = kColsKT + kColsPad;
+
+template <int MT>
+__global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
+  __shared__ __attribute__((aligned(16))) half_t s_w[kColsNT * kColsLd];
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int lr = lane % 16, lg = lane / 16;
+  const int c0 = blockIdx.x * kColsNT;
+  const int rg = blockIdx.y;
+  const int K = *a.n_groups_sel * a.G;
+  int rpg = (K + a.RG - 1) / a.RG;
+  rpg = (rpg + kColsKT - 1) / kColsKT * kColsKT;
+  const int kb0 = min(K, rg * rpg);
+  const int kend = min(K, kb0 + rpg);
+  const half_t* W = reinterpret_cast<const half_t*>(a.W);
+  // tile loader: thread -> rows (tid/16) and (tid/16 + 16), 8 columns at c0 + 8*(tid%16)
+  const int tr = tid / 16, tc = tid % 16;
+  const int col = c0 + 8 * tc;
+  const bool colv = col < a.d;
+  auto row_of = [&](int k) -> long long {
+    if (k >= kend) return -1;
+    const int g = k / a.G;
+    const int grp = a.sel[g];
+    if ((unsigned)grp >= (unsigned)a.n_groups) return -1;
+    return (long long)grp * a.G + (k - g * a.G);
+  };
+  f4v acc[2][MT];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[q][mt] = f4v{0.f, 0.f, 0.f, 0.f};
+  for (int kb = kb0; kb < kend; kb += kColsKT) {   // block-uniform
+    u32x4 wt[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const long long r = row_of(kb + tr + 16 * h);
+      wt[h] = (r >= 0 && colv) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + r * a.ld + col))
+                               : u32x4{0u, 0u, 0u, 0u};
+    }
+    // A fragments: coefficients C[b][kb + 8*lg .. +8] of batch rows b = 16*mt + lr
+    h8v cf[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int b = 16 * mt + lr;
+      const int k = kb + 8 * lg;
+      if (b < a.B && k < kend) {
+        const _Float16* cp = a.C + (long long)b * a.ldc + k;
+        if (k + 8 <= kend) {
+          cf[mt] = *reinterpret_cast<const h8v*>(cp);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) cf[mt][e] = (k + e < kend) ? cp[e] : static_cast<_Float16>(0.f);
+        }
+      } else {
+        cf[mt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+    }
+    __syncthreads();   // the previous tile's readers are done
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const h8v v = __builtin_bit_cast(h8v, wt[h]);
+      const int kk = tr + 16 * h;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_w[(8 * tc + e) * kColsLd + kk] = v[e];
+    }
+    __syncthreads();
+    // wave wv: column tiles 2*wv and 2*wv + 1
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int cl = (2 * wv + q) * 16 + lr;
+      const h8v bf = *reinterpret_cast<const h8v*>(&s_w[cl * kColsLd + 8 * lg]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cf[mt], bf, acc[q][mt], 0, 0, 0);
+    }
+  }
+  // D layout: lane holds output column lr of its tile, batch rows 16*mt + 4*lg + e
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = c0 + (2 * wv + q) * 16 + lr;
+    if (c >= a.d) continue;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int b = 16 * mt + 4 * lg + e;
+        if (b < a.B) a.partial[((long long)b * a.RG + rg) * a.d + c] = acc[q][mt][e];
+      }
+  }
+}
+
+// o[b][slot][e] (fp32, the row's head order) -> C[b][u*dh + e] (fp16, union order, 0 where
+// head u of the union is not selected by row b).
+__global__ void heads_to_union_kernel(const float* o, int kh, int dh, const int32_t* uh, const int* n_uh,
+                                      const unsigned* hbits, int hwords, int B, _Float16* C, long long ldc) {
+  const int u = blockIdx.x, b = blockIdx.y, e = threadIdx.x;
+  if (u >= *n_uh || e >= dh || b >= B) return;
+  const int h = uh[u];
+  const unsigned* rb = hbits + (long long)b * hwords;
+  float v = 0.f;
+  if (bit_of(rb, h)) v = o[((long long)b * kh + rank_below(rb, h)) * dh + e];
+  C[(long long)b * ldc + (long long)u * dh + e] = static_cast<_Float16>(v);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
+  for (int i = 0; i < a.nprob; ++i)
+    if (a.p[i].n > kUnionMaxN || a.p[i].n <= 0) return hipErrorInvalidValue;
+  int maxk = 1;
+  for (int i = 0; i < a.nprob; ++i) maxk = max(maxk, a.p[i].k);
+  hipLaunchKernelGGL(union_zero_kernel, dim3(64, a.nprob), dim3(256), 0, s, a);
+  const long long ent = (long long)a.B * maxk;
+  const int sb = (int)std::min<long long>(1024, (ent + 255) / 256);
+  hipLaunchKernelGGL(union_scatter_kernel, dim3(sb, a.nprob), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(union_list_kernel, dim3(a.nprob), dim3(kUnionBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_norm_f16(const float* x, long long ldx, const float* g, int d, float eps, int B, _Float16* out,
+                                _Float16* out_lo, long long ldo, hipStream_t s) {
+  hipLaunchKernelGGL(rows_norm_f16_kernel, dim3(B), dim3(kNormBlock), 0, s, x, ldx, g, d, eps, out, out_lo, ldo);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_rows(const GemmRowsArgs& a, int max_rows, hipStream_t s) {
+  if (a.d % 8 != 0 || a.B < 1 || a.B > kBatchMax) return hipErrorInvalidValue;   // tail K steps are guarded
+  const int tiles = (max_rows + 15) / 16;
+  const int blocks = max(1, (tiles + 3) / 4);
+  const bool split = a.X_lo != nullptr;
+  if (a.B <= 16) {
+    if (split) hipLaunchKernelGGL((gemm_rows_kernel<1, true>), dim3(blocks), dim3(kGemmBlock), 0, s, a);
+    else hipLaunchKernelGGL((gemm_rows_kernel<1, false>), dim3(blocks), dim3(kGemmBlock), 0, s, a);
+  } else {
+    if (split) hipLaunchKernelGGL((gemm_rows_kernel<2, true>), dim3(blocks), dim3(kGemmBlock), 0, s, a);
+    else hipLaunchKernelGGL((gemm_rows_kernel<2, false>), dim3(blocks), dim3(kGemmBlock), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+int gemm_cols_rg(int d, int max_rows, int B, int cus) {
+  const int ctiles = (d + kColsNT - 1) / kColsNT;
+  int rg = (3 * cus + ctiles - 1) / ctiles;               // about three blocks per CU
+  const int cap = max(1, max_rows / (4 * kColsKT));       // at least 4 tiles of rows per group
+  rg = min(rg, cap);
+  rg = min(rg, kBatchMaxRG);
+  while (rg > 1 && (long long)rg * B > 1024) --rg;        // bounds the partial buffer
+  return max(rg, 1);
+}
+
+hipError_t launch_gemm_cols(const GemmColsArgs& a, hipStream_t s) {
+  if (a.d % 8 != 0 || a.B < 1 || a.B > kBatchMax || a.RG < 1 || a.RG > kBatchMaxRG) return hipErrorInvalidValue;
+  const dim3 grid((a.d + kColsNT - 1) / kColsNT, a.RG);
+  if (a.B <= 16) hipLaunchKernelGGL((gemm_cols_kernel<1>), grid, dim3(kGemmBlock), 0, s, a);
+  else hipLaunchKernelGGL((gemm_cols_kernel<2>), grid, dim3(kGemmBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_heads_to_union(const float* o, int kh, int dh, const int32_t* uh, const int* n_uh, const unsigned* hbits,
+                                 int hwords, int B, int max_uh, _Float16* C, long long ldc, hipStream_t s) {
+  if (dh > 1024 || max_uh < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(heads_to_union_kernel, dim3(max_uh, B), dim3(dh), 0, s, o, kh, dh, uh, n_uh, hbits, hwords, B, C, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace dv

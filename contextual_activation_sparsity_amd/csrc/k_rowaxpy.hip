@@ -135,22 +135,24 @@ __global__ __launch_bounds__(kAxpyBlock) void rowaxpy_part_kernel(RowAxpyArgs a)
   }
 }
 
-// out[b][c] = sum_rg partial[b][rg][c] (group order) + bias[c] + resid[b][c]; 4 columns per
+// out[b][c] = sum_rg partial[b][rg][c] (group order; none if partial is null) + bias[c] + resid[b][c]; 4 columns per
 // thread, small blocks so the few hundred KB of partials are read by many CUs at once.
 constexpr int kReduceBlock = 64;
 __global__ __launch_bounds__(kReduceBlock) void rowaxpy_reduce_kernel(RowAxpyArgs a) {
   const int b = blockIdx.y;
   const int c0 = (blockIdx.x * kReduceBlock + threadIdx.x) * 4;
   if (c0 >= a.d) return;
-  const float* p = a.partial + (long long)b * a.RG * a.d + c0;
-  f32x4 v[kAxpyMaxRG];
-#pragma unroll
-  for (int r = 0; r < kAxpyMaxRG; ++r)
-    if (r < a.RG) v[r] = *reinterpret_cast<const f32x4*>(p + (long long)r * a.d);
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if (a.partial != nullptr) {   // no partials: bias + residual only
+    const float* p = a.partial + (long long)b * a.RG * a.d + c0;
+    f32x4 v[kAxpyMaxRG];
 #pragma unroll
-  for (int r = 0; r < kAxpyMaxRG; ++r)
-    if (r < a.RG) s += v[r];
+    for (int r = 0; r < kAxpyMaxRG; ++r)
+      if (r < a.RG) v[r] = *reinterpret_cast<const f32x4*>(p + (long long)r * a.d);
+#pragma unroll
+    for (int r = 0; r < kAxpyMaxRG; ++r)
+      if (r < a.RG) s += v[r];
+  }
   if (a.bias) s += *reinterpret_cast<const f32x4*>(a.bias + c0);
   if (a.resid) s += *reinterpret_cast<const f32x4*>(a.resid + (long long)b * a.ldr + c0);
   *reinterpret_cast<f32x4*>(a.out + (long long)b * a.ldo + c0) = s;
@@ -181,6 +183,11 @@ hipError_t launch_rowaxpy(const RowAxpyArgs& a, bool f16, int tpc, int B, hipStr
   else hipLaunchKernelGGL((rowaxpy_part_kernel<float, kAxpyTpc>), grid, dim3(kAxpyBlock), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.RG == 1) return e;
+  return launch_axpy_reduce(a, B, s);
+}
+
+hipError_t launch_axpy_reduce(const RowAxpyArgs& a, int B, hipStream_t s) {
+  if (a.RG < 1 || a.RG > kAxpyMaxRG || a.d % 4 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rowaxpy_reduce_kernel, dim3((a.d / 4 + kReduceBlock - 1) / kReduceBlock, B),
                      dim3(kReduceBlock), 0, s, a);
   return hipGetLastError();

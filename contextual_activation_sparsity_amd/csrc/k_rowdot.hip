@@ -33,8 +33,12 @@ constexpr int kRowdotBlock = 256;
 #define DV_ROWDOT_WAVES_PER_EU 1  // lower bound on resident waves per SIMD the registers must allow
 #endif
 
+#ifndef DV_ROWDOT_RMID
+#define DV_ROWDOT_RMID 4     // rows in flight per row-slot when a thread holds 3 or 4 chunks
+#endif
+
 __host__ __device__ constexpr int rowdot_rows_in_flight(int ch) {
-  return ch >= 5 ? DV_ROWDOT_RBIG : (ch >= 3 ? 4 : (ch == 2 ? 6 : 8));
+  return ch >= 5 ? DV_ROWDOT_RBIG : (ch >= 3 ? DV_ROWDOT_RMID : (ch == 2 ? 6 : 8));
 }
 
 // TAG only separates launch sites in profiles (1 = head-sparse q/k/v projection).

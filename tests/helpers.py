@@ -5,7 +5,8 @@ Tolerances (written here, used by every GPU test):
 * top-k index sets: bit-exact on identical fp32 scores;
 * layer outputs: max-abs error <= 2e-2 * RMS(ref) for fp16 weights (fp32 accumulation),
   applied separately to y_a, y_m and the layer output; and the tighter internal bars
-  FP16_BAR / FP32_BAR derived from fp32 accumulation error.
+  FP16_BAR / FP32_BAR derived from fp32 accumulation error, BATCHED_BAR where a batch of
+  two or more rows runs on the matrix cores with fp16 activations.
 """
 from __future__ import annotations
 
@@ -19,6 +20,9 @@ NORTH_STAR_TOL = 2e-2
 FP16_BAR = 1e-3
 FP32_BAR = 1e-4
 SCORE_TOL = 1e-3
+# Batched path (B >= 2, fp16 weights): activations are rounded to fp16 for the matrix cores
+# (2^-11 relative per operand, through the q/k/v, attention, ReLU and both projections).
+BATCHED_BAR = 4e-3
 
 LAYER_KEYS = ("g1", "g2", "wqkv", "bqkv", "wo", "bo", "w1t", "b1", "w2", "b2")
 PRED_KEYS = ("p1_mlp", "p2_mlp", "p1_head", "p2_head")
@@ -55,13 +59,15 @@ def rms(a) -> float:
     return float(np.sqrt(np.mean(a * a))) if a.size else 0.0
 
 
-def assert_close(got, ref, dtype: str, what: str):
+def assert_close(got, ref, dtype: str, what: str, batch: int = 1):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     scale = max(rms(ref), 1e-30)
     err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
     bar = FP16_BAR if dtype == "f16" else FP32_BAR
+    if dtype == "f16" and batch >= 2:
+        bar = BATCHED_BAR
     assert err <= NORTH_STAR_TOL * scale, f"{what}: max-abs {err:.3e} > {NORTH_STAR_TOL} * RMS {scale:.3e}"
     assert err <= bar * scale, f"{what}: max-abs {err:.3e} > internal bar {bar} * RMS {scale:.3e}"
     return err / scale

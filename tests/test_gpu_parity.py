@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import synth
-from helpers import (W_C1, W_C2, W_RAG16, W_RAG32, assert_close, assert_scores_close, dims_of, kv_host,
+from helpers import (BATCHED_BAR, W_C1, W_C2, W_RAG16, W_RAG32, assert_close, assert_scores_close, dims_of, kv_host,
                      layer_weights, pred_weights, random_sets, rms, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -121,7 +121,7 @@ def test_sparse_mlp(dv, host_layers, w, case):
     got = y.cpu().numpy()
     if case == "empty":
         assert np.array_equal(got, np.broadcast_to(t["b2"], got.shape))
-    assert_close(got, ref, w.dtype, f"y_m[{case}]")
+    assert_close(got, ref, w.dtype, f"y_m[{case}]", batch=B)
     if case == "positive":
         dense = oracle.mlp(xn, t["w1t"], t["b1"], t["w2"], t["b2"], np.ones((1, F)))["y_m"]
         assert_close(got, dense, w.dtype, "positive set vs dense")
@@ -168,7 +168,7 @@ def test_sparse_attn(dv, host_layers, w, case):
     got = y.cpu().numpy()
     if case == "empty":
         assert np.array_equal(got, np.broadcast_to(t["bo"], got.shape))
-    assert_close(got, ref["y_a"], w.dtype, f"y_a[{case}]")
+    assert_close(got, ref["y_a"], w.dtype, f"y_a[{case}]", batch=B)
     # cache: selected heads gain the current k, v at slot t_past; nothing else changes
     kg, vg = kcd.cpu().numpy(), vcd.cpu().numpy()
     T = wc.t_past
@@ -179,8 +179,10 @@ def test_sparse_attn(dv, host_layers, w, case):
                     # the slot holds the fp32 projection rounded to the storage type
                     r = ref["qkv"][b, h, m]
                     ulp = 2.0 ** -10 if w.dtype == "f16" else 2.0 ** -23
+                    # batched rows project fp16-rounded inputs on the matrix cores
+                    floor = BATCHED_BAR if (w.dtype == "f16" and B >= 2) else 1e-4
                     err = np.abs(got_c[b, h, T].astype(np.float64) - r)
-                    assert np.all(err <= ulp * np.abs(r) + 1e-4 * rms(r)), f"appended {name}"
+                    assert np.all(err <= ulp * np.abs(r) + floor * rms(r)), f"appended {name}"
                     assert np.max(err) <= 2e-2 * rms(r), f"appended {name}: north-star bar"
 
                     kg_ = got_c[b, h].copy()
@@ -227,8 +229,8 @@ def test_layer_step_given_sets(dv, host_layers, w, B):
     assert np.array_equal(io, S) and np.array_equal(ho, Sh)
     wc = batched(w, B)
     ref = oracle.layer(x, t, kv_host(wc, "k_cache"), kv_host(wc, "v_cache"), w.t_past, S, Sh)
-    assert_close(got, ref["out"], w.dtype, "layer out")
-    assert_close(got - ref["h1"], ref["y_m"], w.dtype, "layer y_m")
+    assert_close(got, ref["out"], w.dtype, "layer out", batch=B)
+    assert_close(got - ref["h1"], ref["y_m"], w.dtype, "layer y_m", batch=B)
 
 
 @pytest.mark.parametrize("w", WORKLOADS, ids=IDS)
