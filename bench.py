@@ -76,6 +76,10 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--workload", choices=["stack", "batched", "sweep"], default="stack",
+                    help="stack: the 24-layer OPT-175B-shaped decode step (default); batched: one "
+                         "OPT-175B-shaped layer at batch 1..32 with Zipf-skewed selections; sweep: the "
+                         "OPT-66B-shaped layer over MLP x head densities")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
@@ -91,6 +95,10 @@ def main() -> int:
     import synth.device as sdev
 
     dv.require_gpu()
+    if args.workload != "stack":
+        out = (run_batched if args.workload == "batched" else run_sweep)(args, log)
+        print(json.dumps(out), flush=True)
+        return 0
     w = synth.OPT175B_STACK.with_(n_layers=args.layers)
     L = w.n_layers
     dims = dv.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, w.t_max, w.dtype)
@@ -314,6 +322,187 @@ def dense_baselines(dv, w, dims, layers, kcs, vcs, xs, n_steps, log):
     log(f"[bench] dense torch layer: {us_t:.1f} us/layer-token")
     del wo_t, w2_t
     return res
+
+
+def timed_single_layer(step, n_steps, log):
+    """Median and quartiles of one step's time (HIP events on the current stream), with an
+    untimed 1 GiB write between steps so no weight stays in the 256 MB Infinity Cache."""
+    import numpy as np
+    import torch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    step(0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step(0)
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(n_steps):
+        step(i)   # host-side input rotation only: the device work is the graph
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    del flush
+    ts = np.array(ts)
+    return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
+
+
+def run_batched(args, log):
+    """One OPT-175B-shaped layer (KV 1024 per sequence) at batch 1..32. Each row's sets are
+    the top-k of Zipf(1.1)-skewed popularity scores (Gumbel-top-k: weighted sampling without
+    replacement); the step is the batched predictor, the top-k of those scores and the
+    layer on the rows' sets (union of the rows' selections on the matrix cores for B >= 2).
+    The dense comparator is the same library with every neuron and head selected."""
+    import numpy as np
+    import torch
+    import contextual_activation_sparsity_amd as dv
+    from contextual_activation_sparsity_amd import traffic
+    import synth
+    import synth.device as sdev
+    w = synth.OPT175B_BATCHED
+    Bmax = 32
+    dims = dv.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, w.t_max, w.dtype)
+    t = sdev.layer_on_device(w, 0)
+    lw = dv.LayerWeights(**{k: t[k] for k in ("g1", "g2", "wqkv", "bqkv", "wo", "bo", "w1t", "b1", "w2", "b2")})
+    pw = dv.PredictorWeights(**{k: t[k] for k in ("p1_mlp", "p2_mlp", "p1_head", "p2_head")})
+    wb = w.with_(batch=Bmax)
+    kc = sdev.kv_on_device(wb, "k_cache", 0)
+    vc = sdev.kv_on_device(wb, "v_cache", 0)
+    steps = max(5, min(args.steps, 30))
+    points = []
+    for B in (1, 2, 4, 8, 16, 32):
+        wB = w.with_(batch=B)
+        zs_m = torch.from_numpy(synth.zipf_scores(wB, w.d_ffn, "sel_mlp")).cuda()
+        zs_h = torch.from_numpy(synth.zipf_scores(wB, w.n_heads, "sel_head")).cuda()
+        idx = torch.empty(B, w.k, dtype=torch.int32, device="cuda")
+        heads = torch.empty(B, w.kh, dtype=torch.int32, device="cuda")
+        dv.dv_topk(zs_m, w.k, idx)
+        dv.dv_topk(zs_h, w.kh, heads)
+        torch.cuda.synchronize()
+        nU = int(np.unique(idx.cpu().numpy()).size)
+        nUh = int(np.unique(heads.cpu().numpy()).size)
+        xs = torch.empty(steps, B, w.d_model, device="cuda")
+        for i in range(steps):
+            sdev.fill_(xs[i], w.key("x", 0, i), w.x_sigma)
+        x = torch.empty(B, w.d_model, device="cuda")
+        y = torch.empty_like(x)
+        s_m = torch.empty(B, w.d_ffn, device="cuda")
+        s_h = torch.empty(B, w.n_heads, device="cuda")
+        ws = dv.workspace(dims, B, w.k, w.kh)
+        tws_m = torch.empty(dv.dv_topk_workspace_bytes(B, w.d_ffn), dtype=torch.uint8, device="cuda")
+        tws_h = torch.empty(dv.dv_topk_workspace_bytes(B, w.n_heads), dtype=torch.uint8, device="cuda")
+        kB, vB = kc[:B], vc[:B]
+
+        def step(i):
+            if torch.cuda.is_current_stream_capturing():
+                dv.dv_predict(dims, pw, x, s_m, s_h, ws)
+                dv.dv_topk(zs_m, w.k, idx, tws_m)
+                dv.dv_topk(zs_h, w.kh, heads, tws_h)
+                dv.dv_layer_step(dims, lw, None, x, None, w.k, w.kh, idx, heads, kB, vB, w.t_past, y, ws=ws)
+            else:
+                x.copy_(xs[i % steps])
+
+        med, p10, p90 = timed_single_layer(step, steps, log)
+        tb = traffic.step_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.t_past, nU, nUh, 2, batch=B,
+                                kh_rows_kv=B * w.kh)
+        # dense comparator: every neuron and head for every row, same library
+        ai = torch.arange(w.d_ffn, dtype=torch.int32, device="cuda").repeat(B, 1).contiguous()
+        ah = torch.arange(w.n_heads, dtype=torch.int32, device="cuda").repeat(B, 1).contiguous()
+        wsd = dv.workspace(dims, B, w.d_ffn, w.n_heads)
+
+        def dstep(i):
+            if torch.cuda.is_current_stream_capturing():
+                dv.dv_layer_step(dims, lw, None, x, None, w.d_ffn, w.n_heads, ai, ah, kB, vB, w.t_past, y, ws=wsd)
+            else:
+                x.copy_(xs[i % steps])
+
+        dmed, _, _ = timed_single_layer(dstep, max(3, steps // 3), log)
+        del wsd, ai, ah
+        pt = {"batch": B, "union_neurons": nU, "union_heads": nUh, "us_per_step": round(med, 2),
+              "us_p10": round(p10, 2), "us_p90": round(p90, 2), "us_per_token": round(med / B, 2),
+              "bytes_per_step": int(tb["total"]), "achieved_GBps": round(tb["total"] / (med * 1e-6) / 1e9, 1),
+              "dense_us_per_step": round(dmed, 2), "speedup_vs_dense": round(dmed / med, 3)}
+        log(f"[bench] batched B={B}: {pt}")
+        points.append(pt)
+        del ws, xs
+        torch.cuda.empty_cache()
+    return {"metric": "us per batched sparse decode step (predictor + top-k + layer), OPT-175B shape",
+            "value": points[-1]["us_per_step"], "unit": "us/step", "n_gpus": 1, "steps": steps,
+            "higher_is_better": False, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "opt175b-shaped layer, batch 1..32, Zipf(1.1) selections, KV 1024",
+                       "k": w.k, "kh": w.kh, "rank": w.rank,
+                       "timing": "median of per-step HIP events over graph replays, 1 GiB write between steps"},
+            "points": points}
+
+
+def run_sweep(args, log):
+    """OPT-66B-shaped layer (KV 2048, rank 1000) at batch 1 over MLP densities x head
+    densities: the full step with inline prediction (predictor, top-k, sparse layer), fresh
+    x per step, against the dense layer through the same library."""
+    import torch
+    import contextual_activation_sparsity_amd as dv
+    from contextual_activation_sparsity_amd import traffic
+    import synth
+    import synth.device as sdev
+    w = synth.OPT66B_LAYER
+    dims = dv.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, w.t_max, w.dtype)
+    t = sdev.layer_on_device(w, 0)
+    lw = dv.LayerWeights(**{k: t[k] for k in ("g1", "g2", "wqkv", "bqkv", "wo", "bo", "w1t", "b1", "w2", "b2")})
+    pw = dv.PredictorWeights(**{k: t[k] for k in ("p1_mlp", "p2_mlp", "p1_head", "p2_head")})
+    kc = sdev.kv_on_device(w, "k_cache", 0)
+    vc = sdev.kv_on_device(w, "v_cache", 0)
+    steps = max(5, min(args.steps, 30))
+    xs = torch.empty(steps, 1, w.d_model, device="cuda")
+    for i in range(steps):
+        sdev.fill_(xs[i], w.key("x", 0, i), w.x_sigma)
+    x = torch.empty(1, w.d_model, device="cuda")
+    y = torch.empty_like(x)
+    points = []
+    for dm in synth.SWEEP_MLP:
+        for dhd in synth.SWEEP_HEAD:
+            k, kh = synth.count_at(dm, w.d_ffn), synth.count_at(dhd, w.n_heads)
+            ws = dv.workspace(dims, 1, k, kh)
+
+            def step(i):
+                if torch.cuda.is_current_stream_capturing():
+                    dv.dv_layer_step(dims, lw, pw, x, x, k, kh, None, None, kc, vc, w.t_past, y, ws=ws)
+                else:
+                    x.copy_(xs[i % steps])
+
+            med, p10, p90 = timed_single_layer(step, steps, log)
+            tb = traffic.step_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.t_past, k, kh, 2)
+            pt = {"mlp_density": dm, "head_density": dhd, "k": k, "kh": kh, "us": round(med, 2),
+                  "us_p10": round(p10, 2), "us_p90": round(p90, 2), "bytes": int(tb["total"]),
+                  "achieved_GBps": round(tb["total"] / (med * 1e-6) / 1e9, 1)}
+            log(f"[bench] sweep {pt}")
+            points.append(pt)
+    idx = torch.arange(w.d_ffn, dtype=torch.int32, device="cuda")[None].contiguous()
+    heads = torch.arange(w.n_heads, dtype=torch.int32, device="cuda")[None].contiguous()
+    wsd = dv.workspace(dims, 1, w.d_ffn, w.n_heads)
+
+    def dstep(i):
+        if torch.cuda.is_current_stream_capturing():
+            dv.dv_layer_step(dims, lw, None, x, None, w.d_ffn, w.n_heads, idx, heads, kc, vc, w.t_past, y, ws=wsd)
+        else:
+            x.copy_(xs[i % steps])
+
+    dmed, _, _ = timed_single_layer(dstep, steps, log)
+    dbytes = traffic.dense_layer_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.t_past, 2)
+    at5 = next(p for p in points if p["mlp_density"] == 0.05 and p["head_density"] == 0.20)
+    return {"metric": "us per sparse decode layer-token over MLP x head density, OPT-66B shape",
+            "value": at5["us"], "unit": "us/layer-token", "n_gpus": 1, "steps": steps, "higher_is_better": False,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "opt66b-shaped layer density sweep, batch 1, inline prediction, KV 2048",
+                       "timing": "median of per-step HIP events over graph replays, 1 GiB write between steps"},
+            "dense": {"us": round(dmed, 2), "bytes": int(dbytes),
+                      "achieved_GBps": round(dbytes / (dmed * 1e-6) / 1e9, 1)},
+            "points": points}
 
 
 def cpu_baseline(w, log):

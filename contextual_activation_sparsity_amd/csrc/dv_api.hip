@@ -241,8 +241,11 @@ dv_status run_predict_stage2(const dv_dims* d, const dv_predictor* P, int B, flo
                              const float* z, int cus, hipStream_t st);
 
 // The batched path (union of the rows' selections on the matrix cores) serves fp16 weights
-// and 2..32 rows; other batches run every row through the single-row kernels.
-bool batched(const dv_dims* d, int B) { return B >= 2 && B <= dv::kBatchMax && is_f16(d); }
+// and 8..32 rows; other batches run every row through the single-row kernels.
+#ifndef DV_BATCH_MIN
+#define DV_BATCH_MIN 8   // measured crossover at OPT-175B shape: below it, rows run one by one faster
+#endif
+bool batched(const dv_dims* d, int B) { return B >= DV_BATCH_MIN && B <= dv::kBatchMax && is_f16(d); }
 
 dv::GemmRowsArgs rows_args(const void* W, long long ld, int dlen, const int32_t* sel, const int* nsel, int G,
                            int n_groups, int B, const _Float16* X, long long ldx) {
@@ -256,7 +259,7 @@ dv::GemmRowsArgs rows_args(const void* W, long long ld, int dlen, const int32_t*
 // (x, then z) enter as fp16 high parts plus fp16 remainders, so the scores keep fp32-like
 // precision (the fp16 weights are exact).
 dv_status run_predict_batched(const dv_dims* d, const dv_predictor* P, const float* x, int B, float* s_mlp,
-                              float* s_head, const Layout& L, void* ws, hipStream_t st) {
+                              float* s_head, const Layout& L, void* ws, int cus, hipStream_t st) {
   const int rm = d->rank_mlp, rh = d->rank_head, D = d->d_model;
   _Float16* xh = at<_Float16>(ws, L.xh);
   _Float16* xl = at<_Float16>(ws, L.xl);
@@ -265,22 +268,22 @@ dv_status run_predict_batched(const dv_dims* d, const dv_predictor* P, const flo
   DV_HIP(dv::launch_rows_norm_f16(x, D, nullptr, D, 0.f, B, xh, xl, D, st));
   dv::GemmRowsArgs a = rows_args(P->p1_mlp, D, D, nullptr, nullptr, 1, rm, B, xh, D);
   a.X_lo = xl; a.mode = dv::kGemmOutF16; a.outh = zh; a.outh_lo = zl; a.ldo = rm + rh;
-  DV_HIP(dv::launch_gemm_rows(a, rm, st));
+  DV_HIP(dv::launch_gemm_rows(a, rm, cus, st));
   a = rows_args(P->p1_head, D, D, nullptr, nullptr, 1, rh, B, xh, D);
   a.X_lo = xl; a.mode = dv::kGemmOutF16; a.outh = zh + rm; a.outh_lo = zl + rm; a.ldo = rm + rh;
-  DV_HIP(dv::launch_gemm_rows(a, rh, st));
+  DV_HIP(dv::launch_gemm_rows(a, rh, cus, st));
   a = rows_args(P->p2_mlp, rm, rm, nullptr, nullptr, 1, d->d_ffn, B, zh, rm + rh);
   a.X_lo = zl; a.mode = dv::kGemmOutF32; a.outf = s_mlp; a.ldo = d->d_ffn;
-  DV_HIP(dv::launch_gemm_rows(a, d->d_ffn, st));
+  DV_HIP(dv::launch_gemm_rows(a, d->d_ffn, cus, st));
   a = rows_args(P->p2_head, rh, rh, nullptr, nullptr, 1, d->n_heads, B, zh + rm, rm + rh);
   a.X_lo = zl + rm; a.mode = dv::kGemmOutF32; a.outf = s_head; a.ldo = d->n_heads;
-  DV_HIP(dv::launch_gemm_rows(a, d->n_heads, st));
+  DV_HIP(dv::launch_gemm_rows(a, d->n_heads, cus, st));
   return DV_OK;
 }
 
 dv_status run_predict(const dv_dims* d, const dv_predictor* P, const float* x, int B, float* s_mlp,
                       float* s_head, const Layout& L, void* ws, int cus, hipStream_t st) {
-  if (batched(d, B)) return run_predict_batched(d, P, x, B, s_mlp, s_head, L, ws, st);
+  if (batched(d, B)) return run_predict_batched(d, P, x, B, s_mlp, s_head, L, ws, cus, st);
   float* z = at<float>(ws, L.z);
   const bool f16 = is_f16(d);
   dv::RowDotArgs a{};
@@ -417,7 +420,7 @@ dv_status run_attn_batched(const dv_dims* d, const dv_layer* Lw, const float* x,
     dv::GemmRowsArgs q = rows_args(Lw->wqkv, D, D, at<int32_t>(ws, L.uhlist), counts + 1, 3 * dh, H, B, xh, D);
     q.bias = Lw->bqkv; q.rowbits = at<unsigned>(ws, L.hbits); q.bits_words = hw;
     q.mode = dv::kGemmOutQkv; q.outf = qkv; q.kh = kh;
-    DV_HIP(dv::launch_gemm_rows(q, L.max_uh * 3 * dh, st));
+    DV_HIP(dv::launch_gemm_rows(q, L.max_uh * 3 * dh, cus, st));
   }
   if (ev_after_qkv) DV_HIP(hipEventRecord(ev_after_qkv, st));
   if (kh > 0) {
@@ -472,7 +475,7 @@ dv_status run_mlp_batched(const dv_dims* d, const dv_layer* Lw, const float* x, 
   dv::GemmRowsArgs a = rows_args(Lw->w1t, D, D, at<int32_t>(ws, L.ulist), counts, 1, F, B, xh, D);
   a.bias = Lw->b1; a.relu = 1; a.rowbits = at<unsigned>(ws, L.ubits); a.bits_words = (F + 31) / 32;
   a.mode = dv::kGemmOutF16; a.outh = cu; a.ldo = L.max_u;
-  DV_HIP(dv::launch_gemm_rows(a, L.max_u, st));
+  DV_HIP(dv::launch_gemm_rows(a, L.max_u, cus, st));
   dv::GemmColsArgs c{};
   c.W = Lw->w2; c.ld = D; c.d = D; c.sel = at<int32_t>(ws, L.ulist); c.n_groups_sel = counts; c.G = 1; c.n_groups = F;
   c.B = B; c.C = cu; c.ldc = L.max_u; c.partial = r.partial; c.RG = dv::gemm_cols_rg(D, L.max_u, B, cus);

@@ -176,7 +176,7 @@ struct GemmRowsArgs {                // out[b][i] = act(W[row_i] . X[b] + bias[r
   long long ldo;
   int kh;                            // slots per row (kGemmOutQkv)
 };
-hipError_t launch_gemm_rows(const GemmRowsArgs& a, int max_rows, hipStream_t s);
+hipError_t launch_gemm_rows(const GemmRowsArgs& a, int max_rows, int cus, hipStream_t s);
 
 struct GemmColsArgs {                // partial[b][rg][c] = sum_k C[b][k] W[row_k][c], MFMA
   const void* W;                     // fp16 rows [n_groups * G][ld]

@@ -111,7 +111,8 @@ __global__ __launch_bounds__(kUnionBlock) void union_list_kernel(UnionArgs a) {
 // RMSNorm of each row (or a plain copy when g is null), rounded to fp16; with out_lo the
 // rounding remainder goes there too (v = hi + lo to about 22 bits, for the split products)
 // ---------------------------------------------------------------------------
-constexpr int kNormBlock = 256;
+constexpr int kNormBlock = 1024;
+constexpr int kNormPT = 4;   // f32x4 chunks per thread per sweep, all loads issued together
 __global__ __launch_bounds__(kNormBlock) void rows_norm_f16_kernel(const float* x, long long ldx, const float* g, int d,
                                                                     float eps, _Float16* out, _Float16* out_lo,
                                                                     long long ldo) {
@@ -119,9 +120,17 @@ __global__ __launch_bounds__(kNormBlock) void rows_norm_f16_kernel(const float* 
   const int b = blockIdx.x, tid = threadIdx.x;
   const float* xb = x + (long long)b * ldx;
   float ss = 0.f;
-  for (int c = tid * 4; c < d; c += kNormBlock * 4) {
-    const f32x4 t = *reinterpret_cast<const f32x4*>(xb + c);
-    ss = fmaf(t[0], t[0], ss); ss = fmaf(t[1], t[1], ss); ss = fmaf(t[2], t[2], ss); ss = fmaf(t[3], t[3], ss);
+  for (int c0 = 0; c0 < d; c0 += kNormBlock * 4 * kNormPT) {
+    f32x4 t[kNormPT];
+#pragma unroll
+    for (int q = 0; q < kNormPT; ++q) {
+      const int c = c0 + (q * kNormBlock + tid) * 4;
+      t[q] = c < d ? *reinterpret_cast<const f32x4*>(xb + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q = 0; q < kNormPT; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = fmaf(t[q][e], t[q][e], ss);
   }
   ss = group_sum<kWave>(ss);
   if (tid % kWave == 0) s_red[tid / kWave] = ss;
@@ -131,15 +140,27 @@ __global__ __launch_bounds__(kNormBlock) void rows_norm_f16_kernel(const float* 
   for (int i = 0; i < kNormBlock / kWave; ++i) tot += s_red[i];
   const float inv = g ? 1.0f / sqrtf(tot / (float)d + eps) : 1.0f;   // no gain: plain cast
   _Float16* ob = out + (long long)b * ldo;
-  for (int c = tid * 4; c < d; c += kNormBlock * 4) {
-    const f32x4 t = *reinterpret_cast<const f32x4*>(xb + c);
-    const f32x4 gg = g ? *reinterpret_cast<const f32x4*>(g + c) : f32x4{1.f, 1.f, 1.f, 1.f};
+  _Float16* lb = out_lo ? out_lo + (long long)b * ldo : nullptr;
+  for (int c0 = 0; c0 < d; c0 += kNormBlock * 4 * kNormPT) {
+    f32x4 t[kNormPT], gg[kNormPT];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float v = t[e] * inv * gg[e];
-      const _Float16 hi = static_cast<_Float16>(v);
-      ob[c + e] = hi;
-      if (out_lo) out_lo[(long long)b * ldo + c + e] = static_cast<_Float16>(v - static_cast<float>(hi));
+    for (int q = 0; q < kNormPT; ++q) {
+      const int c = c0 + (q * kNormBlock + tid) * 4;
+      const bool ok = c < d;
+      t[q] = ok ? *reinterpret_cast<const f32x4*>(xb + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      gg[q] = (ok && g) ? *reinterpret_cast<const f32x4*>(g + c) : f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+#pragma unroll
+    for (int q = 0; q < kNormPT; ++q) {
+      const int c = c0 + (q * kNormBlock + tid) * 4;
+      if (c >= d) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = t[q][e] * inv * gg[q][e];
+        const _Float16 hi = static_cast<_Float16>(v);
+        ob[c + e] = hi;
+        if (lb) lb[c + e] = static_cast<_Float16>(v - static_cast<float>(hi));
+      }
     }
   }
 }
@@ -147,28 +168,38 @@ __global__ __launch_bounds__(kNormBlock) void rows_norm_f16_kernel(const float* 
 // ---------------------------------------------------------------------------
 // gemm_rows: up-projection over gathered rows
 // ---------------------------------------------------------------------------
-constexpr int kGemmBlock = 256;   // 4 waves
-constexpr int kRowsUK = 8;        // K steps (32 each) whose loads are issued together
+constexpr int kGemmBlock = 256;   // 4 waves (gemm_cols)
 
-template <int NT, bool SPLIT>
-__global__ __launch_bounds__(kGemmBlock) void gemm_rows_kernel(GemmRowsArgs a) {
+// A block of KW waves owns MT tiles of 16 gathered rows; its waves split K into KW
+// contiguous ranges, each keeping two batches of UK K-steps of loads in flight. The MT row
+// tiles of a wave share their activation (B) fragments. Partial tiles are summed through
+// LDS in wave order (fixed, so deterministic).
+template <int NT, bool SPLIT, int MT, int KW>
+__global__ __launch_bounds__(KW * kWave) void gemm_rows_kernel(GemmRowsArgs a) {
+  constexpr int UK = MT >= 4 ? 2 : 4;
+  __shared__ float s_acc[KW][MT][NT][4][kWave];
   const int lane = threadIdx.x % kWave;
   const int wv = threadIdx.x / kWave;
   const int nrows = (a.n_groups_sel ? *a.n_groups_sel : a.n_groups) * a.G;
-  const int tile = blockIdx.x * (kGemmBlock / kWave) + wv;
-  const int r0 = tile * 16;
-  if (r0 >= nrows) return;   // whole wave idle (no barriers in this kernel)
+  const int r0 = blockIdx.x * 16 * MT;
+  if (r0 >= nrows) return;   // block-uniform: the whole block leaves before any barrier
   const int lr = lane % 16, lg = lane / 16;
   const half_t* W = reinterpret_cast<const half_t*>(a.W);
-  // A operand: weight row of lane row lr
-  const int ia = r0 + lr;
-  long long wrow = -1;
-  if (ia < nrows) {
-    const int g = ia / a.G;
-    const int grp = a.sel ? a.sel[g] : g;
-    if ((unsigned)grp < (unsigned)a.n_groups) wrow = (long long)grp * a.G + (ia - g * a.G);
+  // A operands: weight row of lane row lr in each of the MT tiles
+  const half_t* wp[MT];
+  bool wok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int ia = r0 + 16 * mt + lr;
+    long long wrow = -1;
+    if (ia < nrows) {
+      const int g = ia / a.G;
+      const int grp = a.sel ? a.sel[g] : g;
+      if ((unsigned)grp < (unsigned)a.n_groups) wrow = (long long)grp * a.G + (ia - g * a.G);
+    }
+    wok[mt] = wrow >= 0;
+    wp[mt] = W + (wrow >= 0 ? wrow : 0) * a.ld + 8 * lg;
   }
-  const half_t* wp = W + (wrow >= 0 ? wrow : 0) * a.ld + 8 * lg;
   const _Float16* xp[NT];
   const _Float16* xq[NT];   // low parts (SPLIT)
   bool xv[NT];
@@ -179,82 +210,135 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_rows_kernel(GemmRowsArgs a) {
     xp[nt] = a.X + (long long)(xv[nt] ? b : 0) * a.ldx + 8 * lg;
     xq[nt] = SPLIT ? a.X_lo + (long long)(xv[nt] ? b : 0) * a.ldx + 8 * lg : nullptr;
   }
-  f4v acc[NT];
+  f4v acc[MT][NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
   const int nk = (a.d + 31) / 32;
-  for (int k0 = 0; k0 < nk; k0 += kRowsUK) {
-    u32x4 av[kRowsUK];
-    h8v bv[kRowsUK][NT];
-    h8v bl[SPLIT ? kRowsUK : 1][NT];
+  const int per = (nk + KW - 1) / KW;
+  const int kbeg = min(nk, wv * per), kend = min(nk, kbeg + per);
+
+  struct Batch {
+    u32x4 av[UK][MT];
+    h8v bv[UK][NT];
+    h8v bl[SPLIT ? UK : 1][NT];
+  };
+  auto load = [&](Batch& q, int k0) {
 #pragma unroll
-    for (int u = 0; u < kRowsUK; ++u) {
+    for (int u = 0; u < UK; ++u) {
       const int ks = k0 + u;
-      const bool ok = ks < nk && ks * 32 + 8 * lg + 8 <= a.d;   // d is a multiple of 8
-      av[u] = (ok && wrow >= 0) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + (long long)ks * 32))
-                                : u32x4{0u, 0u, 0u, 0u};
+      const bool ok = ks < kend && ks * 32 + 8 * lg + 8 <= a.d;   // d is a multiple of 8
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        q.av[u][mt] = (ok && wok[mt]) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[mt] + (long long)ks * 32))
+                                      : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        if (ok && xv[nt]) bv[u][nt] = *reinterpret_cast<const h8v*>(xp[nt] + (long long)ks * 32);
-        else bv[u][nt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+        if (ok && xv[nt]) q.bv[u][nt] = *reinterpret_cast<const h8v*>(xp[nt] + (long long)ks * 32);
+        else q.bv[u][nt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
         if constexpr (SPLIT) {
-          if (ok && xv[nt]) bl[u][nt] = *reinterpret_cast<const h8v*>(xq[nt] + (long long)ks * 32);
-          else bl[u][nt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+          if (ok && xv[nt]) q.bl[u][nt] = *reinterpret_cast<const h8v*>(xq[nt] + (long long)ks * 32);
+          else q.bl[u][nt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
         }
       }
     }
+  };
+  auto mma = [&](const Batch& q) {
 #pragma unroll
-    for (int u = 0; u < kRowsUK; ++u) {
-      const h8v ah = __builtin_bit_cast(h8v, av[u]);
+    for (int u = 0; u < UK; ++u)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const h8v ah = __builtin_bit_cast(h8v, q.av[u][mt]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, q.bv[u][nt], acc[mt][nt], 0, 0, 0);
+          if constexpr (SPLIT)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, q.bl[u][nt], acc[mt][nt], 0, 0, 0);
+        }
+      }
+  };
+  Batch q0, q1;
+  int k0 = kbeg;
+  if (k0 < kend) load(q0, k0);
+  while (k0 < kend) {   // per-wave trip count; no barriers inside
+    const int k1 = k0 + UK;
+    if (k1 < kend) load(q1, k1);
+    mma(q0);
+    k0 = k1;
+    if (k0 >= kend) break;
+    const int k2 = k0 + UK;
+    if (k2 < kend) load(q0, k2);
+    mma(q1);
+    k0 = k2;
+  }
+  // the KW K-ranges of each tile, summed in wave order by wave 0
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_acc[wv][mt][nt][e][lane] = acc[mt][nt][e];
+  __syncthreads();
+  if (wv != 0) return;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = 0.f;
+#pragma unroll
+        for (int w = 0; w < KW; ++w) v += s_acc[w][mt][nt][e][lane];
+        acc[mt][nt][e] = v;
+      }
+  // D layout: lane holds column (batch row) lr of tile nt, gathered rows r0 + 16*mt + 4*lg + e
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = r0 + 16 * mt + 4 * lg + e;
+      if (i >= nrows) continue;
+      const int g = i / a.G;
+      const int wi = i - g * a.G;
+      const int grp = a.sel ? a.sel[g] : g;
+      const bool gv = (unsigned)grp < (unsigned)a.n_groups;
+      const long long row = gv ? (long long)grp * a.G + wi : 0;
+      const float bias = (gv && a.bias) ? a.bias[row] : 0.f;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bv[u][nt], acc[nt], 0, 0, 0);
-        if constexpr (SPLIT) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl[u][nt], acc[nt], 0, 0, 0);
+        const int b = nt * 16 + lr;
+        if (b >= a.B) continue;
+        const unsigned* rb = a.rowbits ? a.rowbits + (long long)b * a.bits_words : nullptr;
+        const bool on = gv && (rb == nullptr || bit_of(rb, grp));
+        float v = acc[mt][nt][e] + bias;
+        if (a.relu) v = fmaxf(v, 0.f);
+        if (a.mode == kGemmOutF16) {
+          const float vv = on ? v : 0.f;
+          const _Float16 hi = static_cast<_Float16>(vv);
+          a.outh[(long long)b * a.ldo + i] = hi;
+          if (a.outh_lo) a.outh_lo[(long long)b * a.ldo + i] = static_cast<_Float16>(vv - static_cast<float>(hi));
+        } else if (a.mode == kGemmOutF32) {
+          a.outf[(long long)b * a.ldo + i] = on ? v : 0.f;
+        } else if (on && rb != nullptr) {   // q/k/v into the row's own slot order
+          const int slot = rank_below(rb, grp);
+          a.outf[((long long)b * a.kh + slot) * a.G + wi] = v;
+        }
       }
     }
-  }
-  // D layout: lane holds column (batch row) lr of tile nt, gathered rows r0 + 4*lg + e
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = r0 + 4 * lg + e;
-    if (i >= nrows) continue;
-    const int g = i / a.G;
-    const int wi = i - g * a.G;
-    const int grp = a.sel ? a.sel[g] : g;
-    const bool gv = (unsigned)grp < (unsigned)a.n_groups;
-    const long long row = gv ? (long long)grp * a.G + wi : 0;
-    const float bias = (gv && a.bias) ? a.bias[row] : 0.f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int b = nt * 16 + lr;
-      if (b >= a.B) continue;
-      const unsigned* rb = a.rowbits ? a.rowbits + (long long)b * a.bits_words : nullptr;
-      const bool on = gv && (rb == nullptr || bit_of(rb, grp));
-      float v = acc[nt][e] + bias;
-      if (a.relu) v = fmaxf(v, 0.f);
-      if (a.mode == kGemmOutF16) {
-        const float vv = on ? v : 0.f;
-        const _Float16 hi = static_cast<_Float16>(vv);
-        a.outh[(long long)b * a.ldo + i] = hi;
-        if (a.outh_lo) a.outh_lo[(long long)b * a.ldo + i] = static_cast<_Float16>(vv - static_cast<float>(hi));
-      } else if (a.mode == kGemmOutF32) {
-        a.outf[(long long)b * a.ldo + i] = on ? v : 0.f;
-      } else if (on && rb != nullptr) {   // q/k/v into the row's own slot order
-        const int slot = rank_below(rb, grp);
-        a.outf[((long long)b * a.kh + slot) * a.G + wi] = v;
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
 // gemm_cols: down-projection over gathered rows, row groups -> partials
 // ---------------------------------------------------------------------------
 constexpr int kColsNT = 128;        // output columns per block (8 MFMA column tiles)
-constexpr int kColsKT = 32;         // gathered rows per LDS tile
+constexpr int kColsKT = 64;         // gathered rows per LDS tile
 constexpr int kColsPad = 8;         // halfs of padding per transposed column
 constexpr int kColsLd = kColsKT + kColsPad;
+constexpr int kColsLoads = kColsKT * kColsNT * 2 / 16 / kGemmBlock;   // 16-byte loads per thread per tile
 
+// The next tile's weight rows are loaded into registers while the current tile is
+// transposed into LDS and consumed, so one tile is always in flight behind the MFMAs.
 template <int MT>
 __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
   __shared__ __attribute__((aligned(16))) half_t s_w[kColsNT * kColsLd];
@@ -268,7 +352,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
   const int kb0 = min(K, rg * rpg);
   const int kend = min(K, kb0 + rpg);
   const half_t* W = reinterpret_cast<const half_t*>(a.W);
-  // tile loader: thread -> rows (tid/16) and (tid/16 + 16), 8 columns at c0 + 8*(tid%16)
+  // tile loader: thread -> rows tr + 16*h (h < kColsLoads), 8 columns at c0 + 8*tc
   const int tr = tid / 16, tc = tid % 16;
   const int col = c0 + 8 * tc;
   const bool colv = col < a.d;
@@ -279,54 +363,79 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
     if ((unsigned)grp >= (unsigned)a.n_groups) return -1;
     return (long long)grp * a.G + (k - g * a.G);
   };
+  auto load_tile = [&](u32x4* wt, int kb) {
+#pragma unroll
+    for (int h = 0; h < kColsLoads; ++h) {
+      const long long r = row_of(kb + tr + 16 * h);
+      wt[h] = (r >= 0 && colv) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + r * a.ld + col))
+                               : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
   f4v acc[2][MT];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[q][mt] = f4v{0.f, 0.f, 0.f, 0.f};
-  for (int kb = kb0; kb < kend; kb += kColsKT) {   // block-uniform
-    u32x4 wt[2];
+  // A fragments of a tile: coefficients C[b][kb + 32*ks + 8*lg .. +8] of batch rows 16*mt + lr
+  auto load_coef = [&](h8v (*cf)[MT], int kb) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const long long r = row_of(kb + tr + 16 * h);
-      wt[h] = (r >= 0 && colv) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + r * a.ld + col))
-                               : u32x4{0u, 0u, 0u, 0u};
-    }
-    // A fragments: coefficients C[b][kb + 8*lg .. +8] of batch rows b = 16*mt + lr
-    h8v cf[MT];
+    for (int ks = 0; ks < kColsKT / 32; ++ks) {
+      const int k = kb + 32 * ks + 8 * lg;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int b = 16 * mt + lr;
-      const int k = kb + 8 * lg;
-      if (b < a.B && k < kend) {
-        const _Float16* cp = a.C + (long long)b * a.ldc + k;
-        if (k + 8 <= kend) {
-          cf[mt] = *reinterpret_cast<const h8v*>(cp);
+      for (int mt = 0; mt < MT; ++mt) {
+        const int b = 16 * mt + lr;
+        if (b < a.B && k < kend) {
+          const _Float16* cp = a.C + (long long)b * a.ldc + k;
+          if (k + 8 <= kend) {
+            cf[ks][mt] = *reinterpret_cast<const h8v*>(cp);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cf[ks][mt][e] = (k + e < kend) ? cp[e] : static_cast<_Float16>(0.f);
+          }
         } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) cf[mt][e] = (k + e < kend) ? cp[e] : static_cast<_Float16>(0.f);
+          cf[ks][mt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
         }
-      } else {
-        cf[mt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
       }
+    }
+  };
+  u32x4 cur[kColsLoads], nxt[kColsLoads];
+  h8v ccur[kColsKT / 32][MT], cnxt[kColsKT / 32][MT];
+  if (kb0 < kend) {
+    load_tile(cur, kb0);
+    load_coef(ccur, kb0);
+  }
+  for (int kb = kb0; kb < kend; kb += kColsKT) {   // block-uniform
+    if (kb + kColsKT < kend) {
+      load_tile(nxt, kb + kColsKT);
+      load_coef(cnxt, kb + kColsKT);
     }
     __syncthreads();   // the previous tile's readers are done
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const h8v v = __builtin_bit_cast(h8v, wt[h]);
+    for (int h = 0; h < kColsLoads; ++h) {
+      const h8v v = __builtin_bit_cast(h8v, cur[h]);
       const int kk = tr + 16 * h;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s_w[(8 * tc + e) * kColsLd + kk] = v[e];
     }
     __syncthreads();
-    // wave wv: column tiles 2*wv and 2*wv + 1
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int cl = (2 * wv + q) * 16 + lr;
-      const h8v bf = *reinterpret_cast<const h8v*>(&s_w[cl * kColsLd + 8 * lg]);
+    for (int ks = 0; ks < kColsKT / 32; ++ks) {
+      // wave wv: column tiles 2*wv and 2*wv + 1
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cf[mt], bf, acc[q][mt], 0, 0, 0);
+      for (int q = 0; q < 2; ++q) {
+        const int cl = (2 * wv + q) * 16 + lr;
+        const h8v bf = *reinterpret_cast<const h8v*>(&s_w[cl * kColsLd + 32 * ks + 8 * lg]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ccur[ks][mt], bf, acc[q][mt], 0, 0, 0);
+      }
     }
+#pragma unroll
+    for (int h = 0; h < kColsLoads; ++h) cur[h] = nxt[h];
+#pragma unroll
+    for (int ks = 0; ks < kColsKT / 32; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) ccur[ks][mt] = cnxt[ks][mt];
   }
   // D layout: lane holds output column lr of its tile, batch rows 16*mt + 4*lg + e
 #pragma unroll
@@ -374,29 +483,46 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
 
 hipError_t launch_rows_norm_f16(const float* x, long long ldx, const float* g, int d, float eps, int B, _Float16* out,
                                 _Float16* out_lo, long long ldo, hipStream_t s) {
+  if (d % 4 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rows_norm_f16_kernel, dim3(B), dim3(kNormBlock), 0, s, x, ldx, g, d, eps, out, out_lo, ldo);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_rows(const GemmRowsArgs& a, int max_rows, hipStream_t s) {
-  if (a.d % 8 != 0 || a.B < 1 || a.B > kBatchMax) return hipErrorInvalidValue;   // tail K steps are guarded
+template <int NT, bool SPLIT>
+static void launch_rows_cfg(const GemmRowsArgs& a, int max_rows, int cus, hipStream_t s) {
+  // more row tiles per wave share the activation fragments; short launches split K over
+  // 8-16 waves per block instead of 4 so that enough waves stream weights
+  constexpr int MTB = NT == 2 ? 4 : 2;
   const int tiles = (max_rows + 15) / 16;
-  const int blocks = max(1, (tiles + 3) / 4);
+  const bool big = (tiles + MTB - 1) / MTB >= cus;
+  if (big && (NT == 2 || a.B > 4)) {
+    hipLaunchKernelGGL((gemm_rows_kernel<NT, SPLIT, MTB, 4>), dim3((tiles + MTB - 1) / MTB), dim3(4 * kWave), 0, s, a);
+  } else if (tiles >= 2 * cus) {
+    hipLaunchKernelGGL((gemm_rows_kernel<NT, SPLIT, 1, 4>), dim3(tiles), dim3(4 * kWave), 0, s, a);
+  } else {   // 16 waves (8 when two batch tiles need the registers)
+    constexpr int KW = NT == 2 ? 8 : 16;
+    hipLaunchKernelGGL((gemm_rows_kernel<NT, SPLIT, 1, KW>), dim3(tiles), dim3(KW * kWave), 0, s, a);
+  }
+}
+
+hipError_t launch_gemm_rows(const GemmRowsArgs& a, int max_rows, int cus, hipStream_t s) {
+  if (a.d % 8 != 0 || a.B < 1 || a.B > kBatchMax || max_rows < 0) return hipErrorInvalidValue;   // tail K steps are guarded
+  if (max_rows == 0) return hipSuccess;
   const bool split = a.X_lo != nullptr;
   if (a.B <= 16) {
-    if (split) hipLaunchKernelGGL((gemm_rows_kernel<1, true>), dim3(blocks), dim3(kGemmBlock), 0, s, a);
-    else hipLaunchKernelGGL((gemm_rows_kernel<1, false>), dim3(blocks), dim3(kGemmBlock), 0, s, a);
+    if (split) launch_rows_cfg<1, true>(a, max_rows, cus, s);
+    else launch_rows_cfg<1, false>(a, max_rows, cus, s);
   } else {
-    if (split) hipLaunchKernelGGL((gemm_rows_kernel<2, true>), dim3(blocks), dim3(kGemmBlock), 0, s, a);
-    else hipLaunchKernelGGL((gemm_rows_kernel<2, false>), dim3(blocks), dim3(kGemmBlock), 0, s, a);
+    if (split) launch_rows_cfg<2, true>(a, max_rows, cus, s);
+    else launch_rows_cfg<2, false>(a, max_rows, cus, s);
   }
   return hipGetLastError();
 }
 
 int gemm_cols_rg(int d, int max_rows, int B, int cus) {
   const int ctiles = (d + kColsNT - 1) / kColsNT;
-  int rg = (3 * cus + ctiles - 1) / ctiles;               // about three blocks per CU
-  const int cap = max(1, max_rows / (4 * kColsKT));       // at least 4 tiles of rows per group
+  int rg = (4 * cus + ctiles - 1) / ctiles;               // about four blocks per CU
+  const int cap = max(1, max_rows / (2 * kColsKT));       // at least 2 tiles of rows per group
   rg = min(rg, cap);
   rg = min(rg, kBatchMaxRG);
   while (rg > 1 && (long long)rg * B > 1024) --rg;        // bounds the partial buffer
