@@ -76,10 +76,11 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=["stack", "batched", "sweep"], default="stack",
+    ap.add_argument("--workload", choices=["stack", "batched", "sweep", "blocked"], default="stack",
                     help="stack: the 24-layer OPT-175B-shaped decode step (default); batched: one "
                          "OPT-175B-shaped layer at batch 1..32 with Zipf-skewed selections; sweep: the "
-                         "OPT-66B-shaped layer over MLP x head densities")
+                         "OPT-66B-shaped layer over MLP x head densities; blocked: per-neuron vs "
+                         "32/64-neuron block selection of the OPT-175B-shaped MLP")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
@@ -96,7 +97,7 @@ def main() -> int:
 
     dv.require_gpu()
     if args.workload != "stack":
-        out = (run_batched if args.workload == "batched" else run_sweep)(args, log)
+        out = {"batched": run_batched, "sweep": run_sweep, "blocked": run_blocked}[args.workload](args, log)
         print(json.dumps(out), flush=True)
         return 0
     w = synth.OPT175B_STACK.with_(n_layers=args.layers)
@@ -502,6 +503,78 @@ def run_sweep(args, log):
                        "timing": "median of per-step HIP events over graph replays, 1 GiB write between steps"},
             "dense": {"us": round(dmed, 2), "bytes": int(dbytes),
                       "achieved_GBps": round(dbytes / (dmed * 1e-6) / 1e9, 1)},
+            "points": points}
+
+
+def run_blocked(args, log):
+    """OPT-175B-shaped MLP at 5 % density: selection + sparse MLP with single neurons
+    (top-k of the scores) against whole blocks of 32 or 64 neurons (top-k of the block
+    maxima), batch 1, per-step HIP events with a 1 GiB write between steps. The scores are
+    synthetic (seeded normal), so the overlap of the two selections says nothing about a
+    trained model; it is reported to show what blocking costs in selection on such scores."""
+    import numpy as np
+    import torch
+    import contextual_activation_sparsity_amd as dv
+    import synth
+    import synth.device as sdev
+    w = synth.OPT175B_BATCHED
+    dims = dv.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, w.t_max, w.dtype)
+    t = sdev.layer_on_device(w, 0)
+    lw = dv.LayerWeights(**{k: t[k] for k in ("g1", "g2", "wqkv", "bqkv", "wo", "bo", "w1t", "b1", "w2", "b2")})
+    steps = max(5, min(args.steps, 30))
+    F, d = w.d_ffn, w.d_model
+    sc = torch.empty(steps, 1, F, device="cuda")
+    xs = torch.empty(steps, 1, d, device="cuda")
+    for i in range(steps):
+        sdev.fill_(sc[i], w.key("scores", 0, i), 1.0)
+        sdev.fill_(xs[i], w.key("x", 0, i), 1.0)
+    s_in = torch.empty(1, F, device="cuda")
+    x = torch.empty(1, d, device="cuda")
+    y = torch.empty_like(x)
+    points = []
+    for bs in (1, 32, 64):
+        kb = max(1, int(round(w.k / bs)))
+        nb = F // bs
+        sel = torch.empty(1, kb, dtype=torch.int32, device="cuda")
+        bsc = torch.empty(1, nb, device="cuda")
+        ws = dv.workspace(dims, 1, kb * bs, 0)
+        tws = torch.empty(dv.dv_topk_workspace_bytes(1, nb), dtype=torch.uint8, device="cuda")
+
+        def step(i):
+            if torch.cuda.is_current_stream_capturing():
+                if bs == 1:
+                    dv.dv_topk(s_in, kb, sel, tws)
+                    dv.dv_sparse_mlp(dims, lw, x, sel, kb, y, ws)
+                else:
+                    dv.dv_block_scores(s_in, bs, bsc)
+                    dv.dv_topk(bsc, kb, sel, tws)
+                    dv.dv_sparse_mlp_blocked(dims, lw, x, sel, kb, bs, y, ws)
+            else:
+                s_in.copy_(sc[i % steps])
+                x.copy_(xs[i % steps])
+
+        med, p10, p90 = timed_single_layer(step, steps, log)
+        # overlap with the per-neuron top-k on the same scores (last step's inputs)
+        s_host = s_in.cpu().numpy()[0]
+        top = set(np.argsort(-s_host, kind="stable")[:w.k].tolist())
+        if bs == 1:
+            kept = 1.0
+        else:
+            chosen = sel.cpu().numpy()[0]
+            neurons = set((chosen[:, None] * bs + np.arange(bs)[None]).ravel().tolist())
+            kept = len(top & neurons) / len(top)
+        mb = 2 * kb * bs * d * 2 / 1e6
+        pt = {"block": bs, "blocks_kept": kb, "neurons_kept": kb * bs, "us": round(med, 2), "us_p10": round(p10, 2),
+              "us_p90": round(p90, 2), "mlp_weight_MB": round(mb, 1),
+              "achieved_GBps_weights": round(mb * 1e6 / (med * 1e-6) / 1e9, 1),
+              "share_of_neuron_topk_kept": round(kept, 4)}
+        log(f"[bench] blocked {pt}")
+        points.append(pt)
+    return {"metric": "us per selection + sparse MLP step, single neurons vs 32/64-neuron blocks, OPT-175B shape",
+            "value": points[0]["us"], "unit": "us/step", "n_gpus": 1, "steps": steps, "higher_is_better": False,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "opt175b-shaped MLP, batch 1, 5 % of neurons, synthetic scores",
+                       "timing": "median of per-step HIP events over graph replays, 1 GiB write between steps"},
             "points": points}
 
 

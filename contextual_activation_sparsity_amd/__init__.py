@@ -25,7 +25,8 @@ from ._lib import DejavuError  # noqa: F401
 
 __all__ = ["Dims", "LayerWeights", "PredictorWeights", "workspace", "stack_workspace", "dv_predict",
            "dv_topk", "dv_sparse_mlp", "dv_sparse_attn", "dv_layer_step", "dv_lookahead_stack",
-           "dv_workspace_bytes", "dv_stack_workspace_bytes", "dv_topk_workspace_bytes", "require_gpu", "DejavuError"]
+           "dv_workspace_bytes", "dv_stack_workspace_bytes", "dv_topk_workspace_bytes", "dv_block_scores",
+           "dv_sparse_mlp_blocked", "require_gpu", "DejavuError"]
 
 _DT = {"f32": (_lib.DV_F32, torch.float32), "f16": (_lib.DV_F16, torch.float16)}
 
@@ -149,6 +150,21 @@ def dv_topk(scores: torch.Tensor, k: int, idx: torch.Tensor, ws: Optional[torch.
     wp, wn = _ws(ws)
     st = _lib.lib().dv_topk(_ptr(scores), B, n, k, _ptr(idx), wp, wn, _stream(stream))
     _lib.check("dv_topk", st)
+
+
+def dv_block_scores(scores: torch.Tensor, bs: int, out: torch.Tensor, stream=None) -> None:
+    B, n = scores.shape
+    st = _lib.lib().dv_block_scores(_ptr(scores), B, n, bs, _ptr(out), _stream(stream))
+    _lib.check("dv_block_scores", st)
+
+
+def dv_sparse_mlp_blocked(dims: Dims, layer: LayerWeights, xn: torch.Tensor, blocks: Optional[torch.Tensor], kb: int,
+                          bs: int, y: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    d, L = dims.c(), layer.c()
+    wp, wn = _ws(ws)
+    st = _lib.lib().dv_sparse_mlp_blocked(ctypes.byref(d), ctypes.byref(L), _ptr(xn), xn.shape[0], _ptr(blocks), kb,
+                                          bs, _ptr(y), wp, wn, _stream(stream))
+    _lib.check("dv_sparse_mlp_blocked", st)
 
 
 def dv_sparse_mlp(dims: Dims, layer: LayerWeights, xn: torch.Tensor, idx: Optional[torch.Tensor], k: int,

@@ -71,6 +71,9 @@ SIGNATURES = {
                                      c_void_p]),
     "dv_workspace_bytes": (c_size_t, [ctypes.POINTER(DvDims), c_int32, c_int32, c_int32]),
     "dv_stack_workspace_bytes": (c_size_t, [ctypes.POINTER(DvDims), c_int32, c_int32, c_int32]),
+    "dv_block_scores": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
+    "dv_sparse_mlp_blocked": (c_int32, [ctypes.POINTER(DvDims), ctypes.POINTER(DvLayer), c_void_p, c_int32, c_void_p,
+                                        c_int32, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "dv_topk_workspace_bytes": (c_size_t, [c_int32, c_int32]),
     "dv_timing_start": (c_int32, [c_int32]),
     "dv_timing_stop": (c_int32, [ctypes.POINTER(ctypes.c_float), c_int32]),

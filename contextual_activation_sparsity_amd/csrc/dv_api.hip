@@ -366,23 +366,25 @@ dv_status run_attn(const dv_dims* d, const dv_layer* Lw, const float* x, const f
   return DV_OK;
 }
 
+// k selected groups of G consecutive neurons each (G = 1: single neurons; G > 1: blocks).
 dv_status run_mlp(const dv_dims* d, const dv_layer* Lw, const float* x, const float* norm_g, int B,
                   const int32_t* idx, int k, float* y, const float* resid, const Layout& L, void* ws, int cus,
-                  hipStream_t st) {
+                  hipStream_t st, int G = 1) {
   const bool f16 = is_f16(d);
   const int D = d->d_model, F = d->d_ffn;
+  const int rows = k * G;
   float* u = at<float>(ws, L.u);
   if (k > 0) {
     dv::RowDotArgs a{};
     a.nseg = 1; a.d = D; a.eps = 1e-5f;
-    a.seg[0] = seg_of(Lw->w1t, D, k, 1, F, idx, k, x, D, norm_g, Lw->b1, u, k, 1);
+    a.seg[0] = seg_of(Lw->w1t, D, rows, G, F / G, idx, k, x, D, norm_g, Lw->b1, u, rows, 1);
     DV_TRY(run_rowdot(a, f16, B, cus, st));
   }
   dv::RowAxpyArgs r{};
   int tpc = 0;
-  dv::rowaxpy_plan(D, k, f16, B, cus, &tpc, &r.n_slices, &r.RG);
-  r.W = Lw->w2; r.ld = D; r.d = D; r.n_rows = k; r.G = 1; r.n_groups = F; r.idx = idx; r.idx_bstride = k;
-  r.coef = u; r.ldc = k; r.bias = Lw->b2; r.resid = resid; r.ldr = D; r.out = y; r.ldo = D;
+  dv::rowaxpy_plan(D, rows, f16, B, cus, &tpc, &r.n_slices, &r.RG);
+  r.W = Lw->w2; r.ld = D; r.d = D; r.n_rows = rows; r.G = G; r.n_groups = F / G; r.idx = idx; r.idx_bstride = k;
+  r.coef = u; r.ldc = rows; r.bias = Lw->b2; r.resid = resid; r.ldr = D; r.out = y; r.ldo = D;
   r.partial = at<float>(ws, L.part);
   DV_HIP(dv::launch_rowaxpy(r, f16, tpc, B, st));
   return DV_OK;
@@ -651,6 +653,34 @@ dv_status dv_sparse_mlp(const dv_dims* dims, const dv_layer* layer, const float*
   DV_TRY(device_info(&di, false));
   if (batched(dims, B)) return run_mlp_batched(dims, layer, xn, nullptr, B, idx, k, y, nullptr, L, ws, di->cus, stream, false);
   return run_mlp(dims, layer, xn, nullptr, B, idx, k, y, nullptr, L, ws, di->cus, stream);
+}
+
+dv_status dv_block_scores(const float* scores, int32_t B, int32_t n, int32_t bs, float* out, hipStream_t stream) {
+  if (B <= 0 || n <= 0) return fail(DV_ERR_DIMS, "B and n must be positive");
+  if (bs < 1 || bs > 4096 || n % bs != 0) return fail(DV_ERR_DIMS, "block size %d must divide n=%d (1..4096)", bs, n);
+  if (scores == nullptr || out == nullptr) return fail(DV_ERR_NULL, "scores and out must be given");
+  DV_TRY(check_ptr(scores, "scores"));   // read as 16-byte chunks when bs % 4 == 0
+  DV_HIP(dv::launch_block_scores(scores, B, n, bs, out, stream));
+  return DV_OK;
+}
+
+dv_status dv_sparse_mlp_blocked(const dv_dims* dims, const dv_layer* layer, const float* xn, int32_t B,
+                                const int32_t* blocks, int32_t kb, int32_t bs, float* y, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  DV_TRY(check_dims(dims));
+  DV_TRY(check_layer(layer, false, true));
+  if (bs < 1 || dims->d_ffn % bs != 0) return fail(DV_ERR_DIMS, "block size %d must divide d_ffn=%d", bs, dims->d_ffn);
+  if (B <= 0) return fail(DV_ERR_DIMS, "batch must be positive");
+  if (kb < 0 || kb > dims->d_ffn / bs) return fail(DV_ERR_K, "kb=%d outside [0, %d]", kb, dims->d_ffn / bs);
+  DV_TRY(check_ptr(xn, "xn"));
+  DV_TRY(check_ptr(y, "y"));
+  if (kb > 0 && blocks == nullptr) return fail(DV_ERR_NULL, "blocks is NULL");
+  const Layout L = layout_of(dims, B, kb * bs, 0);
+  DV_TRY(check_ws(ws, ws_bytes, L.total));
+  DeviceInfo* di;
+  DV_TRY(device_info(&di, false));
+  // whole blocks through the single-row gather kernels (rows of a block are contiguous)
+  return run_mlp(dims, layer, xn, nullptr, B, blocks, kb, y, nullptr, L, ws, di->cus, stream, bs);
 }
 
 dv_status dv_sparse_attn(const dv_dims* dims, const dv_layer* layer, const float* xn, int32_t B,

@@ -199,4 +199,7 @@ hipError_t launch_heads_to_union(const float* o, int kh, int dh, const int32_t* 
 // out[b][c] = sum_rg partial[b][rg][c] (group order) + bias[c] + resid[b][c]
 hipError_t launch_axpy_reduce(const RowAxpyArgs& a, int B, hipStream_t s);
 
+// Blocked-channel scores (k_blocked.hip): out[b][j] = max of scores[b][j*bs .. j*bs+bs-1].
+hipError_t launch_block_scores(const float* scores, int B, int n, int bs, float* out, hipStream_t s);
+
 }  // namespace dv

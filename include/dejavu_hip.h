@@ -109,6 +109,21 @@ dv_status dv_sparse_mlp(const dv_dims* dims, const dv_layer* layer, const float*
                         const int32_t* idx, int32_t k, float* y, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* Blocked-channel scores ("Blocked Channel Sparsity": contiguous blocks of neurons are
+ *   loaded whole when they hold a highly active neuron). scores [B][n] fp32 ->
+ *   out [B][n/bs]: the largest member score of each block, NaN counting as lowest (a block of
+ *   NaNs scores -inf). 1 <= bs <= 4096 and n % bs == 0; scores 16-byte aligned. Rank blocks
+ *   with dv_topk. */
+dv_status dv_block_scores(const float* scores, int32_t B, int32_t n, int32_t bs, float* out, hipStream_t stream);
+
+/* Sparse ReLU MLP over whole blocks of bs consecutive neurons (same section).
+ *   blocks [B][kb]: ascending block ids (block j is neurons j*bs .. j*bs+bs-1); the result
+ *   equals dv_sparse_mlp on the expanded neuron list. d_ffn % bs == 0, 0 <= kb <= d_ffn/bs.
+ *   Workspace: dv_workspace_bytes(dims, B, kb * bs, 0). */
+dv_status dv_sparse_mlp_blocked(const dv_dims* dims, const dv_layer* layer, const float* xn, int32_t B,
+                                const int32_t* blocks, int32_t kb, int32_t bs, float* y, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
 /* Head-sparse decode attention ("Head-Pruned Attention Dispatch").
  *   xn [B][d] fp32 (already normalised), heads [B][kh]; k_cache/v_cache [B][H][t_max][dh].
  *   For each active head h: q,k,v = xn . W_h + b_h; k,v are written to slot t_past of head h

@@ -15,7 +15,8 @@ Sources (the pages this follows):
   sections "Mathematical Formulation of Lookahead Predictors" (the two top-k
   mask equations), "Head-Pruned Attention Dispatch", "The Synchronous
   Prediction Dilemma" (the FFN equation), "Step-by-Step Implementation"
-  (predictor, sparse MLP and layer sketch) and "Mathematical Modeling".
+  (predictor, sparse MLP and layer sketch), "Blocked Channel Sparsity" and
+  "Mathematical Modeling".
 * "Deja Vu: How Contextual Sparsity Accelerates LLM Inference by 6x" (a blog
   summary): "What Is Contextual Sparsity?" (sparsity levels, online phase).
 
@@ -25,5 +26,5 @@ names its pins.
 """
 from .dejavu import (  # noqa: F401
     predict, topk, topk_order_key, rmsnorm, qkv_all_heads, attention, mlp, layer, stack_layer,
-    masks_from_sets, RMS_EPS,
+    masks_from_sets, block_scores, expand_blocks, RMS_EPS,
 )

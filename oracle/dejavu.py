@@ -96,6 +96,31 @@ def topk(scores, k: int) -> np.ndarray:
     return out
 
 
+def block_scores(scores, block: int) -> np.ndarray:
+    """Score of every block of `block` consecutive neurons: the largest member score.
+
+    DejaVu Guide, "Blocked Channel Sparsity": neurons are grouped into
+    contiguous blocks and a block is loaded whole when it holds a highly
+    active neuron, so a block ranks by its best member. NaN members count as
+    lowest (a block of NaNs scores -inf). n must be a multiple of block.
+    Pins: block = 1 is the identity; brute force by Python's max(); a block's
+    score bounds every member's.
+    """
+    s = np.atleast_2d(np.asarray(scores, dtype=np.float32))
+    B, n = s.shape
+    if block < 1 or n % block:
+        raise ValueError("n must be a positive multiple of block")
+    s = np.where(np.isnan(s), -np.inf, s)
+    return s.reshape(B, n // block, block).max(axis=2).astype(np.float32)
+
+
+def expand_blocks(blocks, block: int) -> np.ndarray:
+    """Neuron indices of the selected blocks [B][kb] -> [B][kb * block], ascending."""
+    b = np.atleast_2d(np.asarray(blocks, dtype=np.int64))
+    out = (b[:, :, None] * block + np.arange(block)[None, None, :]).reshape(b.shape[0], -1)
+    return np.sort(out, axis=1).astype(np.int32)
+
+
 def masks_from_sets(sets, n: int) -> np.ndarray:
     """0/1 masks [B][n] from index lists [B][k]."""
     sets = np.atleast_2d(np.asarray(sets, dtype=np.int64))

@@ -66,7 +66,7 @@ TENSOR_IDS: Dict[str, int] = {
     "p1_mlp": 1, "p2_mlp": 2, "p1_head": 3, "p2_head": 4,
     "g1": 5, "g2": 6, "wqkv": 7, "bqkv": 8, "wo": 9, "bo": 10,
     "w1t": 11, "b1": 12, "w2": 13, "b2": 14,
-    "k_cache": 15, "v_cache": 16, "x": 17, "sel_mlp": 18, "sel_head": 19,
+    "k_cache": 15, "v_cache": 16, "x": 17, "sel_mlp": 18, "sel_head": 19, "scores": 20,
 }
 
 

@@ -136,3 +136,18 @@ def test_python_raises_with_status_name():
     with pytest.raises(_lib.DejavuError) as e:
         _lib.check("dv_sparse_mlp", 3)
     assert e.value.status_name == "DV_ERR_K"
+
+
+def test_validation_codes_blocked():
+    f = _lib.lib().dv_block_scores
+    assert f(FAKE, 1, 100, 8, FAKE, None) == 2        # 8 does not divide 100
+    assert f(FAKE, 1, 100, 0, FAKE, None) == 2
+    assert f(None, 1, 100, 4, FAKE, None) == 1
+    assert f(FAKE, 0, 100, 4, FAKE, None) == 2
+    assert f(FAKE + 4, 1, 100, 4, FAKE, None) == 5   # scores not 16-byte aligned
+    g = _lib.lib().dv_sparse_mlp_blocked
+    d, L = dims().c(), layer_struct()
+    assert g(ctypes.byref(d), ctypes.byref(L), FAKE, 1, FAKE, 4, 7, FAKE, FAKE, 1 << 30, None) == 2   # 7 does not divide d_ffn
+    assert g(ctypes.byref(d), ctypes.byref(L), FAKE, 1, FAKE, 3073, 1, FAKE, FAKE, 1 << 30, None) == 3
+    assert g(ctypes.byref(d), ctypes.byref(L), FAKE, 1, None, 4, 8, FAKE, FAKE, 1 << 30, None) == 1
+    assert g(ctypes.byref(d), ctypes.byref(L), FAKE, 1, FAKE, 4, 8, FAKE, FAKE, 16, None) == 7
