@@ -25,6 +25,7 @@ from ._lib import DejavuError  # noqa: F401
 
 __all__ = ["Dims", "LayerWeights", "PredictorWeights", "workspace", "stack_workspace", "dv_predict",
            "dv_topk", "dv_sparse_mlp", "dv_sparse_attn", "dv_layer_step", "dv_lookahead_stack",
+           "dv_decode_step",
            "dv_workspace_bytes", "dv_stack_workspace_bytes", "dv_topk_workspace_bytes", "dv_block_scores",
            "dv_sparse_mlp_blocked", "require_gpu", "DejavuError"]
 
@@ -220,3 +221,27 @@ def dv_lookahead_stack(dims: Dims, layers: Sequence[LayerWeights], preds: Sequen
     st = _lib.lib().dv_lookahead_stack(ctypes.byref(d), Ls, Ps, n, _ptr(x), x.shape[0], k, kh, kcs, vcs, t_past,
                                        _ptr(y), _ptr(h_all), _ptr(idx_out), _ptr(heads_out), wp, wn, main, side)
     _lib.check("dv_lookahead_stack", st)
+
+
+def dv_decode_step(dims: Dims, layers: Sequence[LayerWeights], preds: Sequence[PredictorWeights],
+                   x: torch.Tensor, k: int, kh: int, k_caches: Sequence[torch.Tensor],
+                   v_caches: Sequence[torch.Tensor], t_rows: torch.Tensor, y: torch.Tensor, advance: bool = False,
+                   h_all: Optional[torch.Tensor] = None, idx_out: Optional[torch.Tensor] = None,
+                   heads_out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                   stream=None, side_stream=None) -> None:
+    """t_rows: int32 device tensor [B] of per-row past lengths (advanced in place if advance)."""
+    if t_rows.dtype != torch.int32 or not t_rows.is_cuda or t_rows.numel() != x.shape[0]:
+        raise ValueError("t_rows must be an int32 device tensor with one length per row")
+    n = len(layers)
+    d = dims.c()
+    Ls = (_lib.DvLayer * n)(*[l.c() for l in layers])
+    Ps = (_lib.DvPredictor * n)(*[p.c() for p in preds])
+    kcs = (ctypes.c_void_p * n)(*[_ptr(t) for t in k_caches])
+    vcs = (ctypes.c_void_p * n)(*[_ptr(t) for t in v_caches])
+    wp, wn = _ws(ws)
+    main = _stream(stream)
+    side = main if side_stream is None else side_stream.cuda_stream
+    st = _lib.lib().dv_decode_step(ctypes.byref(d), Ls, Ps, n, _ptr(x), x.shape[0], k, kh, kcs, vcs, _ptr(t_rows),
+                                   int(bool(advance)), _ptr(y), _ptr(h_all), _ptr(idx_out), _ptr(heads_out), wp, wn,
+                                   main, side)
+    _lib.check("dv_decode_step", st)

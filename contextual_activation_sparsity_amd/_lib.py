@@ -69,6 +69,10 @@ SIGNATURES = {
                                      c_int32, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int32,
                                      c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p,
                                      c_void_p]),
+    "dv_decode_step": (c_int32, [ctypes.POINTER(DvDims), ctypes.POINTER(DvLayer), ctypes.POINTER(DvPredictor),
+                                 c_int32, c_void_p, c_int32, c_int32, c_int32, ctypes.POINTER(c_void_p),
+                                 ctypes.POINTER(c_void_p), c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
     "dv_workspace_bytes": (c_size_t, [ctypes.POINTER(DvDims), c_int32, c_int32, c_int32]),
     "dv_stack_workspace_bytes": (c_size_t, [ctypes.POINTER(DvDims), c_int32, c_int32, c_int32]),
     "dv_block_scores": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),

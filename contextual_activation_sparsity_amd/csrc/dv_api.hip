@@ -327,9 +327,16 @@ dv_status run_topk2(const float* s_mlp, int F, int k, int32_t* idx, const float*
   return DV_OK;
 }
 
+// Past KV length: one length t for every row, or per-row lengths on the device (rows) with
+// t their largest allowed value.
+struct KvLen {
+  int t;
+  const int32_t* rows;
+};
+
 // y = resid + (sum over selected heads of o_h . Wo_h + bo), x normalised with norm_g if given.
 dv_status run_attn(const dv_dims* d, const dv_layer* Lw, const float* x, const float* norm_g, int B,
-                   const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* y,
+                   const int32_t* heads, int kh, void* kc, void* vc, KvLen kv, float* y,
                    const float* resid, const Layout& L, void* ws, int cus, hipStream_t st,
                    hipEvent_t ev_after_qkv = nullptr, const dv::RowDotSeg* extra = nullptr, int n_extra = 0) {
   const bool f16 = is_f16(d);
@@ -348,10 +355,10 @@ dv_status run_attn(const dv_dims* d, const dv_layer* Lw, const float* x, const f
   if (ev_after_qkv) DV_HIP(hipEventRecord(ev_after_qkv, st));
   if (kh > 0) {
     dv::AttnArgs at_{};
-    at_.qkv = qkv; at_.heads = heads; at_.kh = kh; at_.n_heads = H; at_.dh = dh; at_.t_past = t_past;
+    at_.qkv = qkv; at_.heads = heads; at_.kh = kh; at_.n_heads = H; at_.dh = dh; at_.t_past = kv.t; at_.t_rows = kv.rows;
     at_.t_max = d->t_max; at_.k_cache = kc; at_.v_cache = vc; at_.partial = at<float>(ws, L.apart);
     at_.o = o;
-    if (!dv::attn_plan(dh, f16, t_past + 1, kh, B, cus, &at_.chunk, &at_.n_chunks))
+    if (!dv::attn_plan(dh, f16, kv.t + 1, kh, B, cus, &at_.chunk, &at_.n_chunks))
       return fail(DV_ERR_DIMS, "head_dim unsupported");
     if (at_.n_chunks > L.max_chunks) return fail(DV_ERR_DIMS, "internal: attention chunk plan");
     DV_HIP(dv::launch_attn(at_, f16, B, st));
@@ -408,7 +415,7 @@ dv_status run_union(const dv_dims* d, int B, const int32_t* idx, int k, const in
 // Batched head-sparse attention: q/k/v over the union of the rows' heads (MFMA), decode
 // attention per (row, selected head), output projection over the union (MFMA) + reduce.
 dv_status run_attn_batched(const dv_dims* d, const dv_layer* Lw, const float* x, const float* norm_g, int B,
-                           const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* y, const float* resid,
+                           const int32_t* heads, int kh, void* kc, void* vc, KvLen kv, float* y, const float* resid,
                            const Layout& L, void* ws, int cus, hipStream_t st, hipEvent_t ev_after_qkv, bool union_done) {
   const int D = d->d_model, dh = d->head_dim, H = d->n_heads;
   const int hw = (H + 31) / 32;
@@ -427,10 +434,10 @@ dv_status run_attn_batched(const dv_dims* d, const dv_layer* Lw, const float* x,
   if (ev_after_qkv) DV_HIP(hipEventRecord(ev_after_qkv, st));
   if (kh > 0) {
     dv::AttnArgs at_{};
-    at_.qkv = qkv; at_.heads = heads; at_.kh = kh; at_.n_heads = H; at_.dh = dh; at_.t_past = t_past;
+    at_.qkv = qkv; at_.heads = heads; at_.kh = kh; at_.n_heads = H; at_.dh = dh; at_.t_past = kv.t; at_.t_rows = kv.rows;
     at_.t_max = d->t_max; at_.k_cache = kc; at_.v_cache = vc; at_.partial = at<float>(ws, L.apart);
     at_.o = o;
-    if (!dv::attn_plan(dh, true, t_past + 1, kh, B, cus, &at_.chunk, &at_.n_chunks))
+    if (!dv::attn_plan(dh, true, kv.t + 1, kh, B, cus, &at_.chunk, &at_.n_chunks))
       return fail(DV_ERR_DIMS, "head_dim unsupported");
     if (at_.n_chunks > L.max_chunks) return fail(DV_ERR_DIMS, "internal: attention chunk plan");
     DV_HIP(dv::launch_attn(at_, true, B, st));
@@ -488,17 +495,17 @@ dv_status run_mlp_batched(const dv_dims* d, const dv_layer* Lw, const float* x, 
 }
 
 dv_status run_layer(const dv_dims* d, const dv_layer* Lw, const float* x, int B, const int32_t* idx, int k,
-                    const int32_t* heads, int kh, void* kc, void* vc, int t_past, float* x_out,
+                    const int32_t* heads, int kh, void* kc, void* vc, KvLen kv, float* x_out,
                     const Layout& L, void* ws, int cus, hipStream_t st, hipEvent_t ev_after_qkv = nullptr,
                     const dv::RowDotSeg* extra = nullptr, int n_extra = 0) {
   float* h1 = at<float>(ws, L.h1);
   if (batched(d, B)) {
     if (n_extra != 0) return fail(DV_ERR_DIMS, "internal: fused segments on the batched path");
     DV_TRY(run_union(d, B, k > 0 ? idx : nullptr, k, kh > 0 ? heads : nullptr, kh, L, ws, st));
-    DV_TRY(run_attn_batched(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, t_past, h1, x, L, ws, cus, st, ev_after_qkv, true));
+    DV_TRY(run_attn_batched(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, kv, h1, x, L, ws, cus, st, ev_after_qkv, true));
     return run_mlp_batched(d, Lw, h1, Lw->g2, B, idx, k, x_out, h1, L, ws, cus, st, true);
   }
-  DV_TRY(run_attn(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, t_past, h1, x, L, ws, cus, st, ev_after_qkv, extra,
+  DV_TRY(run_attn(d, Lw, x, Lw->g1, B, heads, kh, kc, vc, kv, h1, x, L, ws, cus, st, ev_after_qkv, extra,
                   n_extra));
   DV_TRY(run_mlp(d, Lw, h1, Lw->g2, B, idx, k, x_out, h1, L, ws, cus, st));
   return DV_OK;
@@ -698,9 +705,9 @@ dv_status dv_sparse_attn(const dv_dims* dims, const dv_layer* layer, const float
   DeviceInfo* di;
   DV_TRY(device_info(&di, false));
   if (batched(dims, B))
-    return run_attn_batched(dims, layer, xn, nullptr, B, heads, kh, k_cache, v_cache, t_past, y, nullptr, L, ws,
+    return run_attn_batched(dims, layer, xn, nullptr, B, heads, kh, k_cache, v_cache, KvLen{t_past, nullptr}, y, nullptr, L, ws,
                             di->cus, stream, nullptr, false);
-  return run_attn(dims, layer, xn, nullptr, B, heads, kh, k_cache, v_cache, t_past, y, nullptr, L, ws,
+  return run_attn(dims, layer, xn, nullptr, B, heads, kh, k_cache, v_cache, KvLen{t_past, nullptr}, y, nullptr, L, ws,
                   di->cus, stream);
 }
 
@@ -742,16 +749,20 @@ dv_status dv_layer_step(const dv_dims* dims, const dv_layer* layer, const dv_pre
     if (heads_out && kh > 0)
       DV_HIP(hipMemcpyAsync(heads_out, heads_in, sizeof(int32_t) * B * kh, hipMemcpyDeviceToDevice, stream));
   }
-  return run_layer(dims, layer, x, B, idx, k, heads, kh, k_cache, v_cache, t_past, x_out, L, ws, di->cus,
+  return run_layer(dims, layer, x, B, idx, k, heads, kh, k_cache, v_cache, KvLen{t_past, nullptr}, x_out, L, ws, di->cus,
                    stream);
 }
 
-dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const dv_predictor* preds,
-                             int32_t n_layers, const float* x, int32_t B, int32_t k, int32_t kh,
-                             void* const* k_caches, void* const* v_caches, int32_t t_past, float* y, float* h_all,
-                             int32_t* idx_out, int32_t* heads_out, void* ws, size_t ws_bytes, hipStream_t stream,
-                             hipStream_t side_stream) {
-  DV_TRY(check_dims(dims));
+}  // extern "C"
+
+namespace {
+
+// The lookahead stack over KV lengths kv; with advance != null the per-row lengths there
+// are advanced by one once every layer has run (on `stream`, after the last attention).
+dv_status run_stack(const dv_dims* dims, const dv_layer* layers, const dv_predictor* preds, int32_t n_layers,
+                    const float* x, int32_t B, int32_t k, int32_t kh, void* const* k_caches,
+                    void* const* v_caches, KvLen kv, int32_t* advance, float* y, float* h_all, int32_t* idx_out,
+                    int32_t* heads_out, void* ws, size_t ws_bytes, hipStream_t stream, hipStream_t side_stream) {
   if (layers == nullptr || preds == nullptr || k_caches == nullptr || v_caches == nullptr)
     return fail(DV_ERR_NULL, "layers, preds and cache arrays must be given");
   if (n_layers <= 0) return fail(DV_ERR_DIMS, "n_layers must be positive");
@@ -762,7 +773,7 @@ dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const 
   for (int l = 0; l < n_layers; ++l) {
     DV_TRY(check_layer_all(dims, &layers[l]));
     DV_TRY(check_pred(&preds[l]));
-    DV_TRY(check_kv(dims, k_caches[l], v_caches[l], t_past));
+    DV_TRY(check_kv(dims, k_caches[l], v_caches[l], kv.t));
   }
   const Layout L = layout_of(dims, B, k, kh);
   const size_t need = dv_stack_workspace_bytes(dims, B, k, kh);
@@ -818,7 +829,7 @@ dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const 
     dv::RowDotSeg p1[2];
     if (fuse) predict_stage1_segs(dims, &preds[l + 1], h_in(l), at<float>(ws_side, L.z), p1);
     DV_TRY(run_layer(dims, &layers[l], h_in(l), B, sel_idx(l), k, sel_heads(l), kh, k_caches[l], v_caches[l],
-                     t_past, h_outp(l), L, ws, cus, stream, (ahead && two) ? di->ev_in : nullptr,
+                     kv, h_outp(l), L, ws, cus, stream, (ahead && two) ? di->ev_in : nullptr,
                      fuse ? p1 : nullptr, fuse ? 2 : 0));
     if (ahead) {
       if (two) DV_HIP(hipStreamWaitEvent(st_side, di->ev_in, 0));
@@ -832,9 +843,37 @@ dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const 
       if (two) DV_HIP(hipEventRecord(di->ev_sel[(l + 1) % 2], st_side));
     }
   }
+  if (advance) DV_HIP(dv::launch_advance_lengths(advance, B, dims->t_max - 1, stream));
   if (h_all && y != h_all + (size_t)n_layers * B * D)
     DV_HIP(hipMemcpyAsync(y, h_all + (size_t)n_layers * B * D, vecb, hipMemcpyDeviceToDevice, stream));
   return DV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const dv_predictor* preds,
+                             int32_t n_layers, const float* x, int32_t B, int32_t k, int32_t kh,
+                             void* const* k_caches, void* const* v_caches, int32_t t_past, float* y, float* h_all,
+                             int32_t* idx_out, int32_t* heads_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                             hipStream_t side_stream) {
+  DV_TRY(check_dims(dims));
+  return run_stack(dims, layers, preds, n_layers, x, B, k, kh, k_caches, v_caches, KvLen{t_past, nullptr}, nullptr, y,
+                   h_all, idx_out, heads_out, ws, ws_bytes, stream, side_stream);
+}
+
+dv_status dv_decode_step(const dv_dims* dims, const dv_layer* layers, const dv_predictor* preds, int32_t n_layers,
+                         const float* x, int32_t B, int32_t k, int32_t kh, void* const* k_caches,
+                         void* const* v_caches, int32_t* t_rows, int32_t advance, float* y, float* h_all,
+                         int32_t* idx_out, int32_t* heads_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                         hipStream_t side_stream) {
+  DV_TRY(check_dims(dims));
+  if (t_rows == nullptr) return fail(DV_ERR_NULL, "t_rows is NULL");
+  if (reinterpret_cast<uintptr_t>(t_rows) % alignof(int32_t) != 0)
+    return fail(DV_ERR_ALIGN, "t_rows is not 4-byte aligned");
+  return run_stack(dims, layers, preds, n_layers, x, B, k, kh, k_caches, v_caches, KvLen{dims->t_max - 1, t_rows},
+                   advance ? t_rows : nullptr, y, h_all, idx_out, heads_out, ws, ws_bytes, stream, side_stream);
 }
 
 }  // extern "C"

@@ -86,7 +86,8 @@ struct AttnArgs {
   int kh;
   int n_heads;
   int dh;
-  int t_past;
+  int t_past;               // past length of every row; with t_rows: the largest allowed
+  const int32_t* t_rows;    // [B] per-row past lengths on the device, or null
   int t_max;
   void* k_cache;            // [B][H][t_max][dh]
   void* v_cache;
@@ -97,6 +98,8 @@ struct AttnArgs {
 };
 bool attn_plan(int dh, bool f16, int t_total, int kh, int B, int cus, int* chunk, int* n_chunks);
 hipError_t launch_attn(const AttnArgs& a, bool f16, int B, hipStream_t s);
+// t[b] = min(t[b] + 1, cap) for b < B (per-row lengths after a decode step).
+hipError_t launch_advance_lengths(int32_t* t, int B, int cap, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Exact top-k by radix select over many CUs (three kernels, see k_topk.hip).

@@ -6,6 +6,10 @@
 // is the current token, whose k and v come from the fp32 projection and are appended to
 // the cache (rounded to the storage type) by the block that owns that position.
 //
+// Rows may have their own past lengths (a device array read by every block, clamped to
+// [0, bound]); chunks past a row's length see no valid key and leave an empty partial
+// (m = -inf, l = 0) that the combine weighs with zero.
+//
 // Per block: scores s_t = q.K_t / sqrt(dh) with TPK = dh/VEC threads per key (a 16-byte
 // chunk each, summed by an xor butterfly), the chunk maximum m, p_t = exp(s_t - m), the
 // unnormalised p.V in fp32 and l = sum p. Partials (m, l, o) go to the workspace and a
@@ -41,7 +45,7 @@ __global__ __launch_bounds__(kAttnBlock) void attn_kernel(AttnArgs a) {
   const int b = blockIdx.z;
   const int h = a.heads[(long long)b * a.kh + s];
   const bool hv = (unsigned)h < (unsigned)a.n_heads;
-  const int t_past = a.t_past;
+  const int t_past = a.t_rows ? min(max(a.t_rows[b], 0), a.t_past) : a.t_past;
   const float LOG2E = 1.4426950408889634f;
 
   const float* qkv = a.qkv + ((long long)b * a.kh + s) * 3 * DH;
@@ -235,6 +239,17 @@ static hipError_t launch_dh(const AttnArgs& a, int B, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_combine_kernel<DH>), dim3(a.kh, B), dim3(kAttnBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+__global__ void advance_lengths_kernel(int32_t* t, int B, int cap) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) t[b] = min(t[b] + 1, cap);
+}
+
+hipError_t launch_advance_lengths(int32_t* t, int B, int cap, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(advance_lengths_kernel, dim3((B + 63) / 64), dim3(64), 0, s, t, B, cap);
   return hipGetLastError();
 }
 

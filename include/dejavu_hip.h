@@ -164,6 +164,28 @@ dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const 
                              void* ws, size_t ws_bytes, hipStream_t stream,
                              hipStream_t side_stream);
 
+/* One decode token through the lookahead stack, with a past KV length per row held in
+ * device memory, so rows of a batch can sit at different positions and a captured graph of
+ * the call can be replayed for consecutive tokens ("Asynchronous Lookahead Predictors";
+ * the skip of an inactive head's KV from "Head-Pruned Attention Dispatch").
+ *   t_rows [B] int32, DEVICE memory: row b has t_rows[b] past entries in every layer's
+ *   cache and writes the token's k/v at slot t_rows[b] of each head it selects. A head that
+ *   a row does not select leaves that slot as it was (a zero slot of a fresh cache stays
+ *   zero, and later tokens read it as a zero key and value). The kernels read t_rows on the
+ *   device, so the host cannot check it: values outside [0, t_max-1] are clamped into that
+ *   range, which keeps every access inside the cache (the row then attends as if it had
+ *   the clamped length).
+ *   advance != 0: after the last layer, t_rows[b] = min(t_rows[b] + 1, t_max - 1), ordered
+ *   on `stream` after every read of t_rows.
+ *   Everything else is as dv_lookahead_stack (same workspace size); dv_lookahead_stack with
+ *   t_past = T equals this call with every t_rows[b] = T. */
+dv_status dv_decode_step(const dv_dims* dims, const dv_layer* layers, const dv_predictor* preds,
+                         int32_t n_layers, const float* x, int32_t B, int32_t k, int32_t kh,
+                         void* const* k_caches, void* const* v_caches, int32_t* t_rows,
+                         int32_t advance, float* y, float* h_all, int32_t* idx_out,
+                         int32_t* heads_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                         hipStream_t side_stream);
+
 /* Workspace bytes for every single-layer call above at this shape (the maximum). */
 size_t dv_workspace_bytes(const dv_dims* dims, int32_t B, int32_t k, int32_t kh);
 /* Workspace of dv_topk for B rows of n scores (0 if B or n is out of range). */

@@ -151,3 +151,22 @@ def test_validation_codes_blocked():
     assert g(ctypes.byref(d), ctypes.byref(L), FAKE, 1, FAKE, 3073, 1, FAKE, FAKE, 1 << 30, None) == 3
     assert g(ctypes.byref(d), ctypes.byref(L), FAKE, 1, None, 4, 8, FAKE, FAKE, 1 << 30, None) == 1
     assert g(ctypes.byref(d), ctypes.byref(L), FAKE, 1, FAKE, 4, 8, FAKE, FAKE, 16, None) == 7
+
+
+def test_validation_codes_decode_step():
+    f = _lib.lib().dv_decode_step
+    d = dims().c()
+    Ls = (_lib.DvLayer * 1)(layer_struct())
+    Ps = (_lib.DvPredictor * 1)(_lib.DvPredictor(FAKE, FAKE, FAKE, FAKE))
+    kc = (ctypes.c_void_p * 1)(FAKE)
+    vc = (ctypes.c_void_p * 1)(FAKE)
+
+    def call(t_rows, n=1, k=10, ws_bytes=1 << 30):
+        return f(ctypes.byref(d), Ls, Ps, n, FAKE, 1, k, 3, kc, vc, t_rows, 1, FAKE, None, None, None, FAKE,
+                 ws_bytes, None, None)
+
+    assert call(None) == 1                 # per-row lengths are required
+    assert call(FAKE + 2) == 5             # not 4-byte aligned
+    assert call(FAKE, n=0) == 2            # no layers
+    assert call(FAKE, k=3073) == 3         # k above d_ffn
+    assert call(FAKE, ws_bytes=16) == 7    # workspace too small

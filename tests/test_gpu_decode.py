@@ -1,0 +1,233 @@
+"""Multi-step decode on the lookahead stack (GPU): consecutive tokens with a growing KV
+length. Each step appends k/v at slot T only for the heads its row selected; unselected
+heads leave their slot untouched (a zero "hole" that later steps read as a zero key and
+value, DejaVu Guide, "Head-Pruned Attention Dispatch": a skipped head reads and writes none
+of its KV). Every step is checked against the oracle on the cache the step started from
+(teacher forcing), and the two-stream schedule against serial execution over all steps."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import W_RAG16, assert_close, kv_host, layer_weights, pred_weights, to_dev
+
+import contextual_activation_sparsity_amd as dvmod
+
+pytestmark = pytest.mark.gpu
+
+STEPS = 4
+
+
+def padded_cache(w, which, layer):
+    """The past cache of t_past tokens with STEPS zero slots after it (room for the decode)."""
+    c = kv_host(w, which, layer)[:, :, : w.t_past]
+    return np.concatenate([c, np.zeros(c.shape[:2] + (STEPS, c.shape[3]), c.dtype)], axis=2)
+
+
+def run_decode(dv, w, host, two_streams):
+    n = len(host)
+    dev = [to_dev(h) for h in host]
+    dims = dvmod.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, w.t_past + STEPS, w.dtype)
+    kcd = [torch.from_numpy(padded_cache(w, "k_cache", l)).cuda() for l in range(n)]
+    vcd = [torch.from_numpy(padded_cache(w, "v_cache", l)).cuda() for l in range(n)]
+    ws = dv.stack_workspace(dims, w.batch, w.k, w.kh)
+    side = torch.cuda.Stream() if two_streams else None
+    rec = []
+    for s in range(STEPS):
+        T = w.t_past + s
+        before = ([k.cpu().numpy() for k in kcd], [v.cpu().numpy() for v in vcd])
+        x = synth.x_input(w, step=100 + s)
+        xd = torch.from_numpy(x).cuda()
+        y = torch.empty_like(xd)
+        h_all = torch.empty(n + 1, w.batch, w.d_model, device="cuda")
+        io = torch.empty(n, w.batch, w.k, dtype=torch.int32, device="cuda")
+        ho = torch.empty(n, w.batch, w.kh, dtype=torch.int32, device="cuda")
+        dv.dv_lookahead_stack(dims, [layer_weights(t) for t in dev], [pred_weights(t) for t in dev], xd, w.k, w.kh,
+                              kcd, vcd, T, y, h_all=h_all, idx_out=io, heads_out=ho, ws=ws, side_stream=side)
+        torch.cuda.synchronize()
+        after = ([k.cpu().numpy() for k in kcd], [v.cpu().numpy() for v in vcd])
+        rec.append((T, before, after, h_all.cpu().numpy(), io.cpu().numpy(), ho.cpu().numpy()))
+    return rec
+
+
+def test_multi_step_decode_with_kv_holes(dv):
+    w = W_RAG16.with_(t_past=20)
+    n = 2
+    host = [synth.layer_tensors(w, l) for l in range(n)]
+    two = run_decode(dv, w, host, True)
+    one = run_decode(dv, w, host, False)
+    for (T, b2, a2, h2, i2, o2), (_, b1, a1, h1, i1, o1) in zip(two, one):
+        assert np.array_equal(h2, h1) and np.array_equal(i2, i1) and np.array_equal(o2, o1), \
+            f"T={T}: two-stream and serial decode differ"
+        for l in range(n):
+            assert np.array_equal(a2[0][l], a1[0][l]) and np.array_equal(a2[1][l], a1[1][l])
+    holes = 0
+    for T, before, after, h, io, ho in two:
+        for l in range(n):
+            ref = oracle.layer(h[l], host[l], before[0][l], before[1][l], T, io[l], ho[l])
+            assert_close(h[l + 1], ref["out"], w.dtype, f"T={T} layer {l} output")
+            for b in range(w.batch):
+                for hd in range(w.n_heads):
+                    kk, vv = after[0][l][b, hd], after[1][l][b, hd]
+                    if hd in ho[l][b]:
+                        r = ref["qkv"][b, hd]
+                        assert np.max(np.abs(kk[T] - r[1])) <= 2.0 ** -10 * np.max(np.abs(r[1])) + 1e-4
+                        assert np.max(np.abs(vv[T] - r[2])) <= 2.0 ** -10 * np.max(np.abs(r[2])) + 1e-4
+                    else:
+                        assert not kk[T].any() and not vv[T].any(), "an unselected head wrote its slot"
+                        holes += 1
+                    # nothing else in the cache changes
+                    kk2 = kk.copy(); kk2[T] = before[0][l][b, hd, T]
+                    assert np.array_equal(kk2, before[0][l][b, hd])
+    assert holes > 0, "the decode should leave holes for unselected heads"
+
+
+def _stack_inputs(w, n, B, t_max, lengths, seed_step):
+    """Host layers and caches [B][H][t_max][dh] whose row b holds lengths[b] past entries
+    (slots from lengths[b] on are zero, as in a fresh cache)."""
+    host = [synth.layer_tensors(w, l) for l in range(n)]
+    wc = w.with_(batch=B, t_past=t_max - 1)
+    kcs, vcs = [], []
+    for l in range(n):
+        kc, vc = kv_host(wc, "k_cache", l).copy(), kv_host(wc, "v_cache", l).copy()
+        for b, T in enumerate(lengths):
+            kc[b, :, T:] = 0
+            vc[b, :, T:] = 0
+        kcs.append(kc)
+        vcs.append(vc)
+    x = synth.x_input(w.with_(batch=B), step=seed_step)
+    return host, kcs, vcs, x
+
+
+def _run_rows(dv, w, host, kcs, vcs, x, t_max, lengths, advance, side=None, use_stack_T=None):
+    n, B = len(host), x.shape[0]
+    dev = [to_dev(h) for h in host]
+    dims = dvmod.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, t_max, w.dtype)
+    kcd = [torch.from_numpy(a.copy()).cuda() for a in kcs]
+    vcd = [torch.from_numpy(a.copy()).cuda() for a in vcs]
+    xd = torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    h_all = torch.empty(n + 1, B, w.d_model, device="cuda")
+    io = torch.empty(n, B, w.k, dtype=torch.int32, device="cuda")
+    ho = torch.empty(n, B, w.kh, dtype=torch.int32, device="cuda")
+    ws = dv.stack_workspace(dims, B, w.k, w.kh)
+    t_rows = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    if use_stack_T is not None:
+        dv.dv_lookahead_stack(dims, [layer_weights(t) for t in dev], [pred_weights(t) for t in dev], xd, w.k, w.kh,
+                              kcd, vcd, use_stack_T, y, h_all=h_all, idx_out=io, heads_out=ho, ws=ws,
+                              side_stream=side)
+    else:
+        dv.dv_decode_step(dims, [layer_weights(t) for t in dev], [pred_weights(t) for t in dev], xd, w.k, w.kh,
+                          kcd, vcd, t_rows, y, advance=advance, h_all=h_all, idx_out=io, heads_out=ho, ws=ws,
+                          side_stream=side)
+    torch.cuda.synchronize()
+    return (h_all.cpu().numpy(), io.cpu().numpy(), ho.cpu().numpy(), [k.cpu().numpy() for k in kcd],
+            [v.cpu().numpy() for v in vcd], t_rows.cpu().numpy())
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_decode_step_uniform_lengths_equal_stack(dv, B):
+    """Per-row lengths all equal to T give the same bits as the stack called with t_past = T."""
+    w = W_RAG16
+    T, t_max = 30, 33
+    host, kcs, vcs, x = _stack_inputs(w, 2, B, t_max, [T] * B, 7)
+    side = torch.cuda.Stream()
+    a = _run_rows(dv, w, host, kcs, vcs, x, t_max, [T] * B, False, side)
+    b = _run_rows(dv, w, host, kcs, vcs, x, t_max, [T] * B, False, side, use_stack_T=T)
+    for u, v in zip(a[:3], b[:3]):
+        assert np.array_equal(u, v)
+    for l in range(2):
+        assert np.array_equal(a[3][l], b[3][l]) and np.array_equal(a[4][l], b[4][l])
+    assert np.array_equal(a[5], [T] * B)   # no advance asked
+
+
+@pytest.mark.parametrize("lengths", [[0, 5, 20], [3, 0, 31, 17, 9, 22, 1, 30, 12]], ids=["B3-rowwise", "B9-union"])
+def test_ragged_rows_match_oracle_per_row(dv, lengths):
+    """Rows at different positions: each row matches the oracle run on that row alone with
+    its own length, writes its k/v at its own slot only, and the lengths advance by one."""
+    w = W_RAG16
+    B, t_max, n = len(lengths), 32, 2
+    host, kcs, vcs, x = _stack_inputs(w, n, B, t_max, lengths, 9)
+    h, io, ho, kc2, vc2, t_after = _run_rows(dv, w, host, kcs, vcs, x, t_max, lengths, True, torch.cuda.Stream())
+    assert np.array_equal(t_after, [min(T + 1, t_max - 1) for T in lengths])
+    for l in range(n):
+        for b, T in enumerate(lengths):
+            ref = oracle.layer(h[l][b:b + 1], host[l], kcs[l][b:b + 1], vcs[l][b:b + 1], T, io[l][b:b + 1],
+                               ho[l][b:b + 1])
+            assert_close(h[l + 1][b:b + 1], ref["out"], w.dtype, f"row {b} (T={T}) layer {l}",
+                         batch=B if B >= 8 else 1)
+            for hd in range(w.n_heads):
+                changed = np.flatnonzero(np.any(kc2[l][b, hd] != kcs[l][b, hd], axis=-1) |
+                                         np.any(vc2[l][b, hd] != vcs[l][b, hd], axis=-1))
+                assert set(changed.tolist()) <= {T}, f"row {b} head {hd} wrote slots {changed}"
+                if hd not in ho[l][b]:
+                    assert changed.size == 0
+
+
+def test_out_of_range_lengths_are_clamped(dv):
+    """Lengths below 0 or above t_max-1 behave as the clamped values (no access leaves the cache)."""
+    w = W_RAG16
+    t_max = 16
+    host, kcs, vcs, x = _stack_inputs(w, 1, 2, t_max, [0, t_max - 1], 4)
+    a = _run_rows(dv, w, host, kcs, vcs, x, t_max, [-7, t_max + 40], True)
+    b = _run_rows(dv, w, host, kcs, vcs, x, t_max, [0, t_max - 1], True)
+    for u, v in zip(a[:3], b[:3]):
+        assert np.array_equal(u, v)
+    assert np.array_equal(a[3][0], b[3][0]) and np.array_equal(a[4][0], b[4][0])
+    assert np.array_equal(b[5], [1, t_max - 1])   # the advance saturates at t_max-1
+
+
+def test_graph_replay_advances_decode(dv):
+    """One decode step captured in a HIP graph and replayed for consecutive tokens (lengths
+    advanced on the device) gives the bits of eager steps; eager work runs between replays."""
+    w = W_RAG16
+    B, t_max, n, steps = 2, 24, 2, 3
+    lengths = [4, 11]
+    host, kcs, vcs, _ = _stack_inputs(w, n, B, t_max, lengths, 0)
+    xs = [synth.x_input(w.with_(batch=B), step=50 + s) for s in range(steps)]
+    dev = [to_dev(h) for h in host]
+    dims = dvmod.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, t_max, w.dtype)
+    Lw = [layer_weights(t) for t in dev]
+    Pw = [pred_weights(t) for t in dev]
+    side = torch.cuda.Stream()
+
+    def state():
+        return ([torch.from_numpy(a.copy()).cuda() for a in kcs], [torch.from_numpy(a.copy()).cuda() for a in vcs],
+                torch.tensor(lengths, dtype=torch.int32, device="cuda"), torch.empty(n + 1, B, w.d_model, device="cuda"),
+                torch.empty(B, w.d_model, device="cuda"), dv.stack_workspace(dims, B, w.k, w.kh))
+
+    kcE, vcE, tE, hE, yE, wsE = state()
+    eager = []
+    for s in range(steps):
+        dv.dv_decode_step(dims, Lw, Pw, torch.from_numpy(xs[s]).cuda(), w.k, w.kh, kcE, vcE, tE, yE, advance=True,
+                          h_all=hE, ws=wsE, side_stream=side)
+        torch.cuda.synchronize()
+        eager.append(hE.cpu().numpy())
+
+    kcG, vcG, tG, hG, yG, wsG = state()
+    x_in = torch.zeros(B, w.d_model, device="cuda")
+    # warm the library's per-device set-up outside the capture
+    dv.dv_decode_step(dims, Lw, Pw, x_in, w.k, w.kh, [k.clone() for k in kcG], [v.clone() for v in vcG],
+                      tG.clone(), yG, advance=False, ws=wsG, side_stream=side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dv.dv_decode_step(dims, Lw, Pw, x_in, w.k, w.kh, kcG, vcG, tG, yG, advance=True, h_all=hG, ws=wsG,
+                          side_stream=side)
+    torch.cuda.synchronize()
+    # capture records the work without running it: the state is untouched
+    assert np.array_equal(tG.cpu().numpy(), lengths)
+    for s in range(steps):
+        x_in.copy_(torch.from_numpy(xs[s]))
+        g.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(1 << 16, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        del junk
+        assert np.array_equal(hG.cpu().numpy(), eager[s]), f"replay {s} differs from the eager step"
+    assert np.array_equal(tG.cpu().numpy(), tE.cpu().numpy())
+    assert np.array_equal(tG.cpu().numpy(), [T + steps for T in lengths])
+    for l in range(n):
+        assert np.array_equal(kcG[l].cpu().numpy(), kcE[l].cpu().numpy())
+        assert np.array_equal(vcG[l].cpu().numpy(), vcE[l].cpu().numpy())
