@@ -76,11 +76,12 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=["stack", "batched", "sweep", "blocked"], default="stack",
+    ap.add_argument("--workload", choices=["stack", "batched", "sweep", "blocked", "decode"], default="stack",
                     help="stack: the 24-layer OPT-175B-shaped decode step (default); batched: one "
                          "OPT-175B-shaped layer at batch 1..32 with Zipf-skewed selections; sweep: the "
                          "OPT-66B-shaped layer over MLP x head densities; blocked: per-neuron vs "
-                         "32/64-neuron block selection of the OPT-175B-shaped MLP")
+                         "32/64-neuron block selection of the OPT-175B-shaped MLP; decode: consecutive "
+                         "tokens through the 24-layer stack with a growing KV (one graph per token)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
@@ -97,7 +98,8 @@ def main() -> int:
 
     dv.require_gpu()
     if args.workload != "stack":
-        out = {"batched": run_batched, "sweep": run_sweep, "blocked": run_blocked}[args.workload](args, log)
+        out = {"batched": run_batched, "sweep": run_sweep, "blocked": run_blocked,
+               "decode": run_decode}[args.workload](args, log)
         print(json.dumps(out), flush=True)
         return 0
     w = synth.OPT175B_STACK.with_(n_layers=args.layers)
@@ -576,6 +578,117 @@ def run_blocked(args, log):
             "config": {"workload": "opt175b-shaped MLP, batch 1, 5 % of neurons, synthetic scores",
                        "timing": "median of per-step HIP events over graph replays, 1 GiB write between steps"},
             "points": points}
+
+
+def run_decode(args, log):
+    """Consecutive decode tokens through the 24-layer OPT-175B-shaped stack with the KV
+    growing by one slot per token: one call of the stack with per-row lengths on the device
+    is captured once in a HIP graph and replayed per token (the lengths advance on the
+    device, fresh x is copied in before each replay). B = 1 from KV 2048, and B = 8 with
+    the rows spread over KV 256..2048 (union path). Beside it: the fixed-length stack step
+    (graph replay at KV 2048, the same step every time)."""
+    import numpy as np
+    import torch
+    import contextual_activation_sparsity_amd as dv
+    import synth
+    import synth.device as sdev
+    w = synth.OPT175B_STACK
+    L = w.n_layers
+    n_tok = max(8, min(args.steps, 64))
+    warm = 4
+    t_max = w.t_past + n_tok + warm + 1
+    dims = dv.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, t_max, w.dtype)
+    layers, preds = [], []
+    for l in range(L):
+        t = sdev.layer_on_device(w, l)
+        layers.append(dv.LayerWeights(**{k: t[k] for k in ("g1", "g2", "wqkv", "bqkv", "wo", "bo", "w1t", "b1",
+                                                             "w2", "b2")}))
+        preds.append(dv.PredictorWeights(**{k: t[k] for k in ("p1_mlp", "p2_mlp", "p1_head", "p2_head")}))
+    side = torch.cuda.Stream()
+    lines = []
+    for B, lengths in ((1, [w.t_past]), (8, [int(v) for v in np.linspace(256, w.t_past, 8)])):
+        kcs, vcs = [], []
+        for l in range(L):
+            for which, lst in (("k_cache", kcs), ("v_cache", vcs)):
+                c = torch.empty(B, w.n_heads, t_max, w.head_dim, dtype=torch.float16, device="cuda")
+                sdev.fill_(c, w.key(which, l), w.kv_sigma)
+                lst.append(c)
+
+        def reset():
+            for c in kcs + vcs:
+                for b, T in enumerate(lengths):
+                    c[b, :, T:].zero_()
+            t_rows.copy_(torch.tensor(lengths, dtype=torch.int32))
+
+        t_rows = torch.empty(B, dtype=torch.int32, device="cuda")
+        xs = torch.empty(n_tok + warm, B, w.d_model, device="cuda")
+        for i in range(n_tok + warm):
+            sdev.fill_(xs[i], w.key("x", 0, 1000 + i), w.x_sigma)
+        x_in = torch.empty(B, w.d_model, device="cuda")
+        y = torch.empty_like(x_in)
+        ws = dv.stack_workspace(dims, B, w.k, w.kh)
+        reset()
+        x_in.copy_(xs[0])
+        # per-device set-up outside the capture, on scratch copies of the state
+        dv.dv_decode_step(dims, layers, preds, x_in, w.k, w.kh, kcs, vcs, t_rows.clone(), y, advance=False, ws=ws,
+                          side_stream=side)
+        torch.cuda.synchronize()
+        reset()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            dv.dv_decode_step(dims, layers, preds, x_in, w.k, w.kh, kcs, vcs, t_rows, y, advance=True, ws=ws,
+                              side_stream=side)
+        torch.cuda.synchronize()
+        for i in range(warm):
+            x_in.copy_(xs[i])
+            graph.replay()
+        torch.cuda.synchronize()
+        ts = []
+        for i in range(n_tok):
+            x_in.copy_(xs[warm + i])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        t_end = t_rows.cpu().numpy()
+        assert np.array_equal(t_end, np.array(lengths) + warm + n_tok), t_end
+        ts = np.array(ts)
+        line = {"batch": B, "kv_start": lengths, "tokens": n_tok, "us_per_token_median": round(float(np.median(ts)), 2),
+                "us_first": round(float(ts[0]), 2), "us_last": round(float(ts[-1]), 2),
+                "us_per_layer_token": round(float(np.median(ts)) / L / B, 3),
+                "tokens_per_s": round(B * 1e6 / float(np.median(ts)), 1)}
+        # the same shape at a fixed length: the stack step replayed at one position
+        if B == 1:
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2):
+                dv.dv_lookahead_stack(dims, layers, preds, x_in, w.k, w.kh, kcs, vcs, w.t_past, y, ws=ws,
+                                      side_stream=side)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                g2.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(n_tok):
+                g2.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            line["fixed_kv_us_per_token"] = round(e0.elapsed_time(e1) * 1e3 / n_tok, 2)
+            del g2
+        log(f"[bench] decode {line}")
+        lines.append(line)
+        del graph, kcs, vcs, ws, xs
+        torch.cuda.empty_cache()
+    return {"metric": "us per decode token through the 24-layer OPT-175B-shaped stack, KV growing per token",
+            "value": lines[0]["us_per_token_median"], "unit": "us/token", "n_gpus": 1, "steps": n_tok,
+            "higher_is_better": False, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "opt175b-shaped 24-layer stack, consecutive tokens, per-row KV lengths on the "
+                                   "device advanced by the step, one graph replayed per token",
+                       "k": w.k, "kh": w.kh, "rank": w.rank,
+                       "timing": "HIP events around each replay; fresh x copied in before it"},
+            "lines": lines}
 
 
 def cpu_baseline(w, log):
