@@ -16,9 +16,10 @@ Sources (the pages this follows):
   mask equations), "Head-Pruned Attention Dispatch", "The Synchronous
   Prediction Dilemma" (the FFN equation), "Step-by-Step Implementation"
   (predictor, sparse MLP and layer sketch), "Blocked Channel Sparsity" and
-  "Mathematical Modeling".
+  "Mathematical Modeling"; predictor targets in ``train.py``.
 * "Deja Vu: How Contextual Sparsity Accelerates LLM Inference by 6x" (a blog
-  summary): "What Is Contextual Sparsity?" (sparsity levels, online phase).
+  summary): "What Is Contextual Sparsity?" (sparsity levels, online phase; the
+  offline phase that trains the predictors, ``train.py``).
 
 Pinned by tests/test_oracle_*.py against closed forms, invariants, brute force
 on tiny inputs and the printed worked example; each function's docstring
@@ -27,4 +28,7 @@ names its pins.
 from .dejavu import (  # noqa: F401
     predict, topk, topk_order_key, rmsnorm, qkv_all_heads, attention, mlp, layer, stack_layer,
     masks_from_sets, block_scores, expand_blocks, RMS_EPS,
+)
+from .train import (  # noqa: F401
+    layer_labels, sigmoid, bce_logits, predictor_loss_grad, train_predictor, recall,
 )

@@ -67,6 +67,7 @@ TENSOR_IDS: Dict[str, int] = {
     "g1": 5, "g2": 6, "wqkv": 7, "bqkv": 8, "wo": 9, "bo": 10,
     "w1t": 11, "b1": 12, "w2": 13, "b2": 14,
     "k_cache": 15, "v_cache": 16, "x": 17, "sel_mlp": 18, "sel_head": 19, "scores": 20,
+    "x_basis": 21, "x_coef": 22, "x_noise": 23, "labels": 24,
 }
 
 
@@ -201,6 +202,7 @@ class Workload:
     x_sigma: float = 1.0
     kv_sigma: float = 1.0
     bias_sigma: float = 0.0
+    b1_mean: float = 0.0  # added to every up-projection bias (sets how often a neuron fires)
     seed: int = 0
 
     @property
@@ -227,8 +229,15 @@ OPT175B_STACK = Workload("opt175b-stack24-fp16", 4, 12288, 49152, 96, 128, 1000,
 OPT175B_BATCHED = Workload("opt175b-batched-fp16", 5, 12288, 49152, 96, 128, 1000, 1024, 2458, 19,
                            "f16")
 
+# OPT-125m-shaped layer, fp32, for predictor training: up-projection biases shifted to -0.7
+# so that about 10 % of the neurons fire (pre-activation std ~ 0.02 * sqrt(768) = 0.55);
+# k = 10 % of the neurons, kh = 3 of 12 heads. Samples are single tokens (no past KV), so
+# every head's output is its value vector, a function of the sample alone.
+OPT125M_TRAIN = Workload("opt125m-train-fp32", 6, 768, 3072, 12, 64, 128, 0, 307, 3, "f32",
+                         bias_sigma=0.02, b1_mean=-0.7)
+
 WORKLOADS = {w.name: w for w in (OPT125M_LAYER, OPT6P7B_LAYER, OPT66B_LAYER, OPT175B_STACK,
-                                 OPT175B_BATCHED)}
+                                 OPT175B_BATCHED, OPT125M_TRAIN)}
 
 # Density sweep points of the OPT-66B-shaped layer.
 SWEEP_MLP = (0.02, 0.05, 0.10, 0.25, 0.50, 1.00)
@@ -270,6 +279,8 @@ def layer_tensors(w: Workload, layer: int = 0) -> Dict[str, np.ndarray]:
            for name, (shp, sg, dt) in layer_shapes(w).items()}
     out["g1"] = gains(w)
     out["g2"] = gains(w)
+    if w.b1_mean != 0.0:
+        out["b1"] = (out["b1"] + np.float32(w.b1_mean)).astype(np.float32)
     return out
 
 
@@ -308,3 +319,28 @@ def zipf_scores(w: Workload, n: int, tensor_name: str, exponent: float = 1.1) ->
         ub = np.clip(ub, 1e-300, None)
         out[b] = (logw - np.log(-np.log(ub))).astype(np.float32)
     return out
+
+
+def lowdim_x(w: Workload, n: int, dim: int = 32, noise: float = 0.1, mean_sigma: float = 1.0,
+             split: int = 0) -> np.ndarray:
+    """Layer inputs [n][d] fp32 near a seeded affine subspace of dimension dim.
+
+    x = mu + g . U^T + e: a shared mean vector mu (elements of std `mean_sigma`), U [d][dim]
+    of std 1/sqrt(dim) (so each element of g . U^T has variance about 1), coefficients
+    g [n][dim] of std 1 and isotropic noise e of std `noise`. Formed in float64 and rounded
+    once to fp32. `split` selects an independent draw of g and e (0: training samples,
+    1: held-out samples) over the same mu and U. Stands in for hidden states, which have a
+    shared mean direction and low intrinsic dimension; both are what let a linear predictor
+    see which neurons fire and which heads are large.
+    """
+    mu = tensor(w.key("x_basis", 0, 1), (w.d_model,), mean_sigma, "f32").astype(np.float64)
+    u = tensor(w.key("x_basis"), (w.d_model, dim), 1.0 / math.sqrt(dim), "f32").astype(np.float64)
+    g = tensor(w.key("x_coef", 0, split), (n, dim), 1.0, "f32").astype(np.float64)
+    e = tensor(w.key("x_noise", 0, split), (n, w.d_model), noise, "f32").astype(np.float64)
+    return (mu[None] + g @ u.T + e).astype(np.float32)
+
+
+def random_labels(w: Workload, n: int, width: int, p: float, split: int = 0) -> np.ndarray:
+    """0/1 labels [n][width] uint8, each 1 with probability p (independent uniforms)."""
+    u = uniform01(w.key("labels", 0, split), 0, n * width).reshape(n, width)
+    return (u < p).astype(np.uint8)

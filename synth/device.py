@@ -51,6 +51,8 @@ def _tdt(dtype: str) -> torch.dtype:
 
 def layer_on_device(w: Workload, layer: int = 0, device="cuda") -> Dict[str, torch.Tensor]:
     """All tensors of one layer (weights, predictor, gains) drawn in device memory."""
+    if w.b1_mean != 0.0:
+        raise ValueError("layer_on_device draws unshifted biases; use layer_tensors for b1_mean != 0")
     out = {}
     for name, (shp, sg, dt) in layer_shapes(w).items():
         t = torch.empty(shp, dtype=_tdt(dt), device=device)
