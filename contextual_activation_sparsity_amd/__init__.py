@@ -25,7 +25,7 @@ from ._lib import DejavuError  # noqa: F401
 
 __all__ = ["Dims", "LayerWeights", "PredictorWeights", "workspace", "stack_workspace", "dv_predict",
            "dv_topk", "dv_sparse_mlp", "dv_sparse_attn", "dv_layer_step", "dv_lookahead_stack",
-           "dv_decode_step",
+           "dv_decode_step", "dv_layer_labels", "dv_predictor_train_workspace_bytes", "dv_predictor_train_step",
            "dv_workspace_bytes", "dv_stack_workspace_bytes", "dv_topk_workspace_bytes", "dv_block_scores",
            "dv_sparse_mlp_blocked", "require_gpu", "DejavuError"]
 
@@ -166,6 +166,45 @@ def dv_sparse_mlp_blocked(dims: Dims, layer: LayerWeights, xn: torch.Tensor, blo
     st = _lib.lib().dv_sparse_mlp_blocked(ctypes.byref(d), ctypes.byref(L), _ptr(xn), xn.shape[0], _ptr(blocks), kb,
                                           bs, _ptr(y), wp, wn, _stream(stream))
     _lib.check("dv_sparse_mlp_blocked", st)
+
+
+def dv_layer_labels(dims: Dims, layer: LayerWeights, x: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                    t_past: int, fire: Optional[torch.Tensor] = None, preact: Optional[torch.Tensor] = None,
+                    head_norm: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Dense-layer training targets: fire [B][F] uint8, preact [B][F] fp32, head_norm [B][H] fp32."""
+    d, L = dims.c(), layer.c()
+    if ws is None:
+        ws = workspace(dims, x.shape[0], dims.d_ffn, dims.n_heads)
+    wp, wn = _ws(ws)
+    st = _lib.lib().dv_layer_labels(ctypes.byref(d), ctypes.byref(L), _ptr(x), x.shape[0], _ptr(k_cache),
+                                    _ptr(v_cache), t_past, _ptr(fire), _ptr(preact), _ptr(head_norm), wp, wn,
+                                    _stream(stream))
+    _lib.check("dv_layer_labels", st)
+
+
+def dv_predictor_train_workspace_bytes(M: int, d: int, N: int, r: int) -> int:
+    return int(_lib.lib().dv_predictor_train_workspace_bytes(M, d, N, r))
+
+
+def dv_predictor_train_step(x: torch.Tensor, y: torch.Tensor, p1: torch.Tensor, p2: torch.Tensor, v1: torch.Tensor,
+                            v2: torch.Tensor, lr: float, momentum: float, loss: torch.Tensor,
+                            ws: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One full-batch step on x [M][d] fp32, y [M][N] uint8, p1 [r][d], p2 [N][r] (updated in place)."""
+    M, d = x.shape
+    N, r = p2.shape
+    if y.dtype != torch.uint8 or tuple(y.shape) != (M, N) or tuple(p1.shape) != (r, d):
+        raise ValueError("shapes: x [M][d], y [M][N] uint8, p1 [r][d], p2 [N][r]")
+    for name, t in (("x", x), ("p1", p1), ("p2", p2), ("v1", v1), ("v2", v2), ("loss", loss)):
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    if v1.shape != p1.shape or v2.shape != p2.shape:
+        raise ValueError("momentum buffers must match the factors")
+    if ws is None:
+        ws = _alloc_ws(dv_predictor_train_workspace_bytes(M, d, N, r), x.device)
+    wp, wn = _ws(ws)
+    st = _lib.lib().dv_predictor_train_step(_ptr(x), M, d, _ptr(y), N, r, _ptr(p1), _ptr(p2), _ptr(v1), _ptr(v2),
+                                            float(lr), float(momentum), _ptr(loss), wp, wn, _stream(stream))
+    _lib.check("dv_predictor_train_step", st)
 
 
 def dv_sparse_mlp(dims: Dims, layer: LayerWeights, xn: torch.Tensor, idx: Optional[torch.Tensor], k: int,

@@ -73,6 +73,12 @@ SIGNATURES = {
                                  c_int32, c_void_p, c_int32, c_int32, c_int32, ctypes.POINTER(c_void_p),
                                  ctypes.POINTER(c_void_p), c_void_p, c_int32, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "dv_layer_labels": (c_int32, [ctypes.POINTER(DvDims), ctypes.POINTER(DvLayer), c_void_p, c_int32, c_void_p,
+                                  c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "dv_predictor_train_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+    "dv_predictor_train_step": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_int32, c_int32, c_void_p, c_void_p,
+                                          c_void_p, c_void_p, ctypes.c_float, ctypes.c_float, c_void_p, c_void_p,
+                                          c_size_t, c_void_p]),
     "dv_workspace_bytes": (c_size_t, [ctypes.POINTER(DvDims), c_int32, c_int32, c_int32]),
     "dv_stack_workspace_bytes": (c_size_t, [ctypes.POINTER(DvDims), c_int32, c_int32, c_int32]),
     "dv_block_scores": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),

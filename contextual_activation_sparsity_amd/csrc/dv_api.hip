@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <cmath>
 #include <map>
 #include <mutex>
 #include <string>
@@ -688,6 +689,115 @@ dv_status dv_sparse_mlp_blocked(const dv_dims* dims, const dv_layer* layer, cons
   DV_TRY(device_info(&di, false));
   // whole blocks through the single-row gather kernels (rows of a block are contiguous)
   return run_mlp(dims, layer, xn, nullptr, B, blocks, kb, y, nullptr, L, ws, di->cus, stream, bs);
+}
+
+dv_status dv_layer_labels(const dv_dims* dims, const dv_layer* layer, const float* x, int32_t B, void* k_cache,
+                          void* v_cache, int32_t t_past, uint8_t* fire, float* preact, float* head_norm, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  DV_TRY(check_dims(dims));
+  DV_TRY(check_layer_all(dims, layer));
+  if (B <= 0) return fail(DV_ERR_DIMS, "batch must be positive");
+  DV_TRY(check_ptr(x, "x"));
+  DV_TRY(check_kv(dims, k_cache, v_cache, t_past));
+  if (fire == nullptr && preact == nullptr && head_norm == nullptr)
+    return fail(DV_ERR_NULL, "give at least one of fire, preact, head_norm");
+  if (preact != nullptr) DV_TRY(check_ptr(preact, "preact"));
+  if (head_norm != nullptr) DV_TRY(check_ptr(head_norm, "head_norm"));
+  const int D = dims->d_model, F = dims->d_ffn, H = dims->n_heads;
+  const Layout L = layout_of(dims, B, F, H);
+  DV_TRY(check_ws(ws, ws_bytes, L.total));
+  DeviceInfo* di;
+  DV_TRY(device_info(&di, false));
+  // the dense layer's attention block: every head of every row (row-wise kernels)
+  int32_t* heads = at<int32_t>(ws, L.heads);
+  DV_HIP(dv::launch_iota_rows(heads, B, H, stream));
+  float* h1 = at<float>(ws, L.h1);
+  DV_TRY(run_attn(dims, layer, x, layer->g1, B, heads, H, k_cache, v_cache, KvLen{t_past, nullptr}, h1, x, L, ws,
+                  di->cus, stream));
+  if (head_norm) DV_HIP(dv::launch_head_norm(at<float>(ws, L.o), B * H, dims->head_dim, head_norm, stream));
+  // up-projection pre-activations of every neuron on RMSNorm(h1) (identity row list, no ReLU)
+  if (fire != nullptr || preact != nullptr) {
+    float* a = preact ? preact : at<float>(ws, L.u);
+    dv::RowDotArgs r{};
+    r.nseg = 1; r.d = D; r.eps = 1e-5f;
+    r.seg[0] = seg_of(layer->w1t, D, F, 1, F, nullptr, 0, h1, D, layer->g2, layer->b1, a, F, 0);
+    DV_TRY(run_rowdot(r, is_f16(dims), B, di->cus, stream));
+    if (fire) DV_HIP(dv::launch_fire(a, (long long)B * F, fire, stream));
+  }
+  return DV_OK;
+}
+
+namespace {
+struct TrainPlan {
+  int ks[5];                 // K slices of the five products
+  size_t z, s, dz, g1, g2, scratch, part, total;
+};
+
+// The slice plan is fixed (planned for 256 compute units), so a step gives the same bits on
+// any device.
+TrainPlan train_plan(int M, int d, int N, int r) {
+  TrainPlan p{};
+  const int outs[5][3] = {{M, r, d}, {M, N, r}, {N, r, M}, {M, r, N}, {r, d, M}};
+  size_t scratch = 0;
+  for (int i = 0; i < 5; ++i) {
+    p.ks[i] = dv::gemm_f32_slices(outs[i][0], outs[i][1], outs[i][2], 256);
+    if (p.ks[i] > 1) scratch = std::max(scratch, (size_t)p.ks[i] * outs[i][0] * outs[i][1]);
+  }
+  size_t off = 0;
+  auto take = [&](size_t n) { const size_t o = off; off = align256(off + 4 * n); return o; };
+  p.z = take((size_t)M * r);
+  p.s = take((size_t)M * N);
+  p.dz = take((size_t)M * r);
+  p.g1 = take((size_t)r * d);
+  p.g2 = take((size_t)N * r);
+  p.scratch = take(scratch);
+  p.part = take((size_t)dv::loss_parts());
+  p.total = off;
+  return p;
+}
+}  // namespace
+
+size_t dv_predictor_train_workspace_bytes(int32_t M, int32_t d, int32_t N, int32_t r) {
+  if (M <= 0 || d <= 0 || N <= 0 || r <= 0) return 0;
+  return train_plan(M, d, N, r).total;
+}
+
+dv_status dv_predictor_train_step(const float* x, int32_t M, int32_t d, const uint8_t* y, int32_t N, int32_t r,
+                                  float* p1, float* p2, float* v1, float* v2, float lr, float momentum, float* loss,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (M <= 0 || d <= 0 || N <= 0 || r <= 0) return fail(DV_ERR_DIMS, "M, d, N and r must be positive");
+  if (!(lr >= 0.f) || !(momentum >= 0.f) || !std::isfinite(lr) || !std::isfinite(momentum))
+    return fail(DV_ERR_DIMS, "lr and momentum must be finite and non-negative");
+  DV_TRY(check_ptr(x, "x"));
+  DV_TRY(check_ptr(y, "y"));
+  DV_TRY(check_ptr(p1, "p1"));
+  DV_TRY(check_ptr(p2, "p2"));
+  DV_TRY(check_ptr(v1, "v1"));
+  DV_TRY(check_ptr(v2, "v2"));
+  if (loss == nullptr) return fail(DV_ERR_NULL, "loss is NULL");
+  if (reinterpret_cast<uintptr_t>(loss) % alignof(float) != 0) return fail(DV_ERR_ALIGN, "loss is not 4-byte aligned");
+  const TrainPlan P = train_plan(M, d, N, r);
+  DV_TRY(check_ws(ws, ws_bytes, P.total));
+  float* Z = at<float>(ws, P.z);
+  float* S = at<float>(ws, P.s);
+  float* dZ = at<float>(ws, P.dz);
+  float* g1 = at<float>(ws, P.g1);
+  float* g2 = at<float>(ws, P.g2);
+  float* scr = at<float>(ws, P.scratch);
+  // Z = x P1^T  [M][r]
+  DV_HIP(dv::launch_gemm_f32({x, d, 1, p1, 1, d, Z, M, r, d}, P.ks[0], scr, stream));
+  // S = Z P2^T  [M][N]
+  DV_HIP(dv::launch_gemm_f32({Z, r, 1, p2, 1, r, S, M, N, r}, P.ks[1], scr, stream));
+  // G = (sigmoid(S) - y) / (M N) in place, and the loss
+  DV_HIP(dv::launch_bce_grad(S, y, (long long)M * N, at<float>(ws, P.part), loss, stream));
+  // dL/dP2 = G^T Z  [N][r]
+  DV_HIP(dv::launch_gemm_f32({S, 1, N, Z, r, 1, g2, N, r, M}, P.ks[2], scr, stream));
+  // dL/dZ = G P2  [M][r]
+  DV_HIP(dv::launch_gemm_f32({S, N, 1, p2, r, 1, dZ, M, r, N}, P.ks[3], scr, stream));
+  // dL/dP1 = dZ^T x  [r][d]
+  DV_HIP(dv::launch_gemm_f32({dZ, 1, r, x, d, 1, g1, r, d, M}, P.ks[4], scr, stream));
+  DV_HIP(dv::launch_momentum_step(p1, v1, g1, (long long)r * d, p2, v2, g2, (long long)N * r, lr, momentum, stream));
+  return DV_OK;
 }
 
 dv_status dv_sparse_attn(const dv_dims* dims, const dv_layer* layer, const float* xn, int32_t B,

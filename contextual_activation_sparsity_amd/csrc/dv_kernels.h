@@ -205,4 +205,28 @@ hipError_t launch_axpy_reduce(const RowAxpyArgs& a, int B, hipStream_t s);
 // Blocked-channel scores (k_blocked.hip): out[b][j] = max of scores[b][j*bs .. j*bs+bs-1].
 hipError_t launch_block_scores(const float* scores, int B, int n, int bs, float* out, hipStream_t s);
 
+// Predictor training (k_train.hip).
+hipError_t launch_iota_rows(int32_t* out, int rows, int n, hipStream_t s);   // out[b][i] = i
+hipError_t launch_head_norm(const float* o, int BH, int dh, float* norm, hipStream_t s);
+hipError_t launch_fire(const float* a, long long n, uint8_t* fire, hipStream_t s);   // fire = a > 0
+
+// C [M][N] = op(A) op(B) in fp32, A(i,k) = A[i*sai + k*sak], B(k,j) = B[k*sbk + j*sbj].
+struct GemmF32Args {
+  const float* A;
+  long long sai, sak;
+  const float* B;
+  long long sbk, sbj;
+  float* C;
+  int M, N, K;
+};
+constexpr int kGemmMaxSlices = 16;
+int gemm_f32_slices(int M, int N, int K, int cus);   // K slices that fill `cus` compute units
+// With slices > 1, scratch holds slices * M * N floats (partial products summed in slice order).
+hipError_t launch_gemm_f32(GemmF32Args a, int slices, float* scratch, hipStream_t s);
+// S [n] scores -> (sigmoid(S) - y) / n in place; *loss = mean cross-entropy (part: loss_parts() floats).
+hipError_t launch_bce_grad(float* S, const uint8_t* y, long long n, float* part, float* loss, hipStream_t s);
+int loss_parts();
+hipError_t launch_momentum_step(float* p1, float* v1, const float* g1, long long n1, float* p2, float* v2,
+                                const float* g2, long long n2, float lr, float mu, hipStream_t s);
+
 }  // namespace dv

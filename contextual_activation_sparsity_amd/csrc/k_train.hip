@@ -1,0 +1,232 @@
+// Predictor training: targets from the dense layer and gradient steps of the rank-r score map
+// (DejaVu Guide, "Mathematical Formulation of Lookahead Predictors": the head predictor marks
+// the heads with the largest attention norms, the neuron predictor the neurons that fire; blog
+// summary "What Is Contextual Sparsity?": the classifiers are trained offline on the dense
+// model's activations, with the layer input as features).
+//
+// Loss: mean binary cross-entropy of the scores (logits) over every (sample, output) pair;
+// optimiser: full-batch gradient descent with heavy-ball momentum. The contractions are fp32
+// GEMMs on the vector units (fp32 matrix-core and vector peaks are equal on this chip, and
+// these problems are small and off the decode path); every reduction runs in a fixed order, so
+// a step is bitwise reproducible.
+#include <algorithm>
+
+#include "dv_device.h"
+#include "dv_kernels.h"
+
+namespace dv {
+
+constexpr int kGemmTile = 64;
+constexpr int kGemmK = 16;
+constexpr int kGemmThreads = 256;
+constexpr int kLossBlocks = 512;
+
+// ---------------------------------------------------------------------------
+// Targets
+// ---------------------------------------------------------------------------
+__global__ void iota_rows_kernel(int32_t* out, int rows, int n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < (long long)rows * n) out[i] = (int32_t)(i % n);
+}
+
+// ||o_h||_2 for every (row, head); o is [B][H][dh] fp32.
+__global__ void head_norm_kernel(const float* o, int BH, int dh, float* norm) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= BH) return;
+  const float* v = o + (long long)i * dh;
+  float s = 0.f;
+  for (int e = 0; e < dh; ++e) s = fmaf(v[e], v[e], s);
+  norm[i] = sqrtf(s);
+}
+
+__global__ void fire_kernel(const float* a, long long n, uint8_t* fire) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) fire[i] = a[i] > 0.f ? 1 : 0;
+}
+
+hipError_t launch_iota_rows(int32_t* out, int rows, int n, hipStream_t s) {
+  const long long total = (long long)rows * n;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(iota_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, out, rows, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_norm(const float* o, int BH, int dh, float* norm, hipStream_t s) {
+  if (BH <= 0) return hipSuccess;
+  hipLaunchKernelGGL(head_norm_kernel, dim3((BH + 255) / 256), dim3(256), 0, s, o, BH, dh, norm);
+  return hipGetLastError();
+}
+
+hipError_t launch_fire(const float* a, long long n, uint8_t* fire, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fire_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, n, fire);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fp32 GEMM with strided operands: C[i][j] = sum_k A(i,k) B(k,j), A(i,k) = A[i*sai + k*sak],
+// B(k,j) = B[k*sbk + j*sbj]. A 64 x 64 tile per block, K in steps of 16 staged in LDS, 4 x 4
+// outputs per thread. With ksplit > 1, slice z of the K range writes its partial tile to
+// C + z*M*N and a second kernel sums the slices in order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kGemmThreads) void gemm_f32_kernel(GemmF32Args a, int k_per_slice) {
+  __shared__ float As[kGemmK][kGemmTile + 4];
+  __shared__ float Bs[kGemmK][kGemmTile + 4];
+  const int tid = threadIdx.x;
+  const int tx = tid % 16, ty = tid / 16;
+  const int i0 = blockIdx.y * kGemmTile, j0 = blockIdx.x * kGemmTile;
+  const int kb = blockIdx.z * k_per_slice;
+  const int ke = min(a.K, kb + k_per_slice);
+  const bool a_kfast = a.sak == 1;
+  const bool b_jfast = a.sbj == 1;
+  float acc[4][4] = {};
+  for (int k0 = kb; k0 < ke; k0 += kGemmK) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + q * kGemmThreads;
+      const int ii = a_kfast ? e / kGemmK : e % kGemmTile;
+      const int kk = a_kfast ? e % kGemmK : e / kGemmTile;
+      const int gi = i0 + ii, gk = k0 + kk;
+      As[kk][ii] = (gi < a.M && gk < ke) ? a.A[(long long)gi * a.sai + (long long)gk * a.sak] : 0.f;
+      const int jj = b_jfast ? e % kGemmTile : e / kGemmK;
+      const int k2 = b_jfast ? e / kGemmTile : e % kGemmK;
+      const int gj = j0 + jj, gk2 = k0 + k2;
+      Bs[k2][jj] = (gj < a.N && gk2 < ke) ? a.B[(long long)gk2 * a.sbk + (long long)gj * a.sbj] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kGemmK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) av[r] = As[kk][ty * 4 + r];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bv[c] = Bs[kk][tx * 4 + c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+    }
+    __syncthreads();
+  }
+  float* C = a.C + (long long)blockIdx.z * a.M * a.N;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int gi = i0 + ty * 4 + r;
+    if (gi >= a.M) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int gj = j0 + tx * 4 + c;
+      if (gj < a.N) C[(long long)gi * a.N + gj] = acc[r][c];
+    }
+  }
+}
+
+__global__ void sum_slices_kernel(const float* part, int slices, long long n, float* out) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = part[i];
+  for (int z = 1; z < slices; ++z) s += part[(long long)z * n + i];
+  out[i] = s;
+}
+
+int gemm_f32_slices(int M, int N, int K, int cus) {
+  const long long tiles = (long long)((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile);
+  const long long want = 2LL * cus;
+  int ks = (int)std::min<long long>((want + tiles - 1) / tiles, std::max(1, K / 256));
+  return std::max(1, std::min(ks, kGemmMaxSlices));
+}
+
+// C = op(A) op(B); with more than one slice, `scratch` holds slices*M*N floats.
+hipError_t launch_gemm_f32(GemmF32Args a, int slices, float* scratch, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.K <= 0 || slices < 1) return hipErrorInvalidValue;
+  int kps = (a.K + slices - 1) / slices;
+  kps = (kps + kGemmK - 1) / kGemmK * kGemmK;
+  slices = std::max(1, (a.K + kps - 1) / kps);
+  float* dst = a.C;
+  if (slices > 1) a.C = scratch;
+  dim3 grid((a.N + kGemmTile - 1) / kGemmTile, (a.M + kGemmTile - 1) / kGemmTile, slices);
+  hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(kGemmThreads), 0, s, a, std::max(kps, 1));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || slices == 1) return e;
+  const long long n = (long long)a.M * a.N;
+  hipLaunchKernelGGL(sum_slices_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, scratch, slices, n, dst);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Loss and its gradient with respect to the scores, in place: S becomes
+// G = (sigmoid(S) - y) / n. Block b sums softplus(s) - y*s over its contiguous range into
+// part[b]; the finishing kernel adds the parts in block order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bce_grad_kernel(float* S, const uint8_t* y, long long n, float inv_n,
+                                                       long long per_block, float* part) {
+  __shared__ float s_red[256 / kWave];
+  const long long b0 = (long long)blockIdx.x * per_block;
+  const long long b1 = min(n, b0 + per_block);
+  float acc = 0.f;
+  for (long long i = b0 + threadIdx.x; i < b1; i += blockDim.x) {
+    const float s = S[i];
+    const float t = y[i] ? 1.f : 0.f;
+    const float e = expf(-fabsf(s));
+    acc += fmaxf(s, 0.f) + log1pf(e) - t * s;
+    const float sig = s >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+    S[i] = (sig - t) * inv_n;
+  }
+  acc = group_sum<kWave>(acc);
+  if ((threadIdx.x % kWave) == 0) s_red[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < 256 / kWave; ++w) t += s_red[w];
+    part[blockIdx.x] = t;
+  }
+}
+
+__global__ void loss_finish_kernel(const float* part, int n_part, float inv_n, float* loss) {
+  if (threadIdx.x != 0) return;
+  float t = 0.f;
+  for (int i = 0; i < n_part; ++i) t += part[i];
+  *loss = t * inv_n;
+}
+
+hipError_t launch_bce_grad(float* S, const uint8_t* y, long long n, float* part, float* loss, hipStream_t s) {
+  const float inv_n = 1.f / (float)n;
+  const long long per_block = (n + kLossBlocks - 1) / kLossBlocks;
+  hipLaunchKernelGGL(bce_grad_kernel, dim3(kLossBlocks), dim3(256), 0, s, S, y, n, inv_n, per_block, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(loss_finish_kernel, dim3(1), dim3(64), 0, s, part, kLossBlocks, inv_n, loss);
+  return hipGetLastError();
+}
+
+int loss_parts() { return kLossBlocks; }
+
+// v = mu v + g; p = p - lr v, over two parameter arrays in one launch.
+__global__ void momentum_step_kernel(float* p1, float* v1, const float* g1, long long n1, float* p2, float* v2,
+                                     const float* g2, long long n2, float lr, float mu) {
+  long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  float *p, *v;
+  const float* g;
+  if (i < n1) {
+    p = p1; v = v1; g = g1;
+  } else {
+    i -= n1;
+    if (i >= n2) return;
+    p = p2; v = v2; g = g2;
+  }
+  const float vn = fmaf(mu, v[i], g[i]);
+  v[i] = vn;
+  p[i] = p[i] - lr * vn;
+}
+
+hipError_t launch_momentum_step(float* p1, float* v1, const float* g1, long long n1, float* p2, float* v2,
+                                const float* g2, long long n2, float lr, float mu, hipStream_t s) {
+  const long long n = n1 + n2;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(momentum_step_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p1, v1, g1, n1, p2,
+                     v2, g2, n2, lr, mu);
+  return hipGetLastError();
+}
+
+}  // namespace dv

@@ -186,6 +186,41 @@ dv_status dv_decode_step(const dv_dims* dims, const dv_layer* layers, const dv_p
                          int32_t* heads_out, void* ws, size_t ws_bytes, hipStream_t stream,
                          hipStream_t side_stream);
 
+/* Training targets of one layer for the lookahead predictors, from the dense layer (every head
+ * and every neuron selected): DejaVu Guide, "Mathematical Formulation of Lookahead
+ * Predictors" (the head predictor targets the heads with the largest attention norms, the
+ * neuron predictor the neurons that fire); blog summary "What Is Contextual Sparsity?" (the
+ * offline phase records each input's active heads and neurons).
+ *   x [B][d] fp32 layer inputs; caches as dv_sparse_attn (slot t_past of every head is
+ *   written with the input's k/v, as a dense layer step would).
+ *   fire [B][F] uint8 (nullable): 1 where the up-projection pre-activation on RMSNorm(h1),
+ *   h1 = x + Attn(RMSNorm(x)), is positive (ReLU passes it), else 0.
+ *   preact [B][F] fp32 (nullable): those pre-activations (bias included).
+ *   head_norm [B][H] fp32 (nullable): ||o_h||_2 of every head's attention output; the head
+ *   targets are its top-kh per row (dv_topk).
+ *   At least one output must be given. Workspace: dv_workspace_bytes(dims, B, d_ffn,
+ *   n_heads). */
+dv_status dv_layer_labels(const dv_dims* dims, const dv_layer* layer, const float* x, int32_t B,
+                          void* k_cache, void* v_cache, int32_t t_past, uint8_t* fire, float* preact,
+                          float* head_norm, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One full-batch training step of a rank-r predictor (blog summary "What Is Contextual
+ * Sparsity?": a small classifier per layer, trained on the layer's input; the scores of
+ * "Mathematical Formulation of Lookahead Predictors" are its logits). All fp32, device memory:
+ *   x [M][d] inputs, y [M][N] uint8 0/1 targets, p1 [r][d] and p2 [N][r] the two factors
+ *   (scores s = (x p1^T) p2^T), v1/v2 their momentum buffers (zero before the first step).
+ *   Loss: mean binary cross-entropy of s against y over all M*N pairs; *loss (device) gets
+ *   its value at the parameters before the update. Update (heavy-ball momentum):
+ *   v <- momentum * v + grad, p <- p - lr * v, for both factors.
+ *   x, y, p1, p2, v1, v2 16-byte aligned; loss 4-byte aligned.
+ *   Deterministic: the same inputs give the same bits on any device. Workspace:
+ *   dv_predictor_train_workspace_bytes(M, d, N, r). */
+size_t dv_predictor_train_workspace_bytes(int32_t M, int32_t d, int32_t N, int32_t r);
+dv_status dv_predictor_train_step(const float* x, int32_t M, int32_t d, const uint8_t* y, int32_t N,
+                                  int32_t r, float* p1, float* p2, float* v1, float* v2, float lr,
+                                  float momentum, float* loss, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* Workspace bytes for every single-layer call above at this shape (the maximum). */
 size_t dv_workspace_bytes(const dv_dims* dims, int32_t B, int32_t k, int32_t kh);
 /* Workspace of dv_topk for B rows of n scores (0 if B or n is out of range). */

@@ -170,3 +170,29 @@ def test_validation_codes_decode_step():
     assert call(FAKE, n=0) == 2            # no layers
     assert call(FAKE, k=3073) == 3         # k above d_ffn
     assert call(FAKE, ws_bytes=16) == 7    # workspace too small
+
+
+def test_validation_codes_training():
+    f = _lib.lib().dv_predictor_train_step
+    g = _lib.lib().dv_predictor_train_workspace_bytes
+    assert g(0, 8, 8, 2) == 0 and g(8, 8, 8, -1) == 0
+    need = g(64, 32, 16, 4)
+    assert need > 4 * (64 * 16 + 2 * 64 * 4) and need % 256 == 0
+
+    def call(M=64, d=32, N=16, r=4, lr=0.1, mu=0.9, x=FAKE, loss=FAKE, ws_bytes=1 << 30):
+        return f(x, M, d, FAKE, N, r, FAKE, FAKE, FAKE, FAKE, lr, mu, loss, FAKE, ws_bytes, None)
+
+    assert call(M=0) == 2
+    assert call(lr=float("nan")) == 2
+    assert call(mu=-0.5) == 2
+    assert call(x=None) == 1
+    assert call(x=FAKE + 4) == 5
+    assert call(loss=FAKE + 2) == 5       # the loss slot needs 4-byte alignment only
+    assert call(ws_bytes=need - 1) == 7
+    h = _lib.lib().dv_layer_labels
+    d = dims().c()
+    L = layer_struct()
+    assert h(ctypes.byref(d), ctypes.byref(L), FAKE, 2, FAKE, FAKE, 0, None, None, None, FAKE, 1 << 30, None) == 1
+    assert h(ctypes.byref(d), ctypes.byref(L), FAKE, 0, FAKE, FAKE, 0, FAKE, None, None, FAKE, 1 << 30, None) == 2
+    assert h(ctypes.byref(d), ctypes.byref(L), FAKE, 2, FAKE, FAKE, 129, FAKE, None, None, FAKE, 1 << 30, None) == 6
+    assert h(ctypes.byref(d), ctypes.byref(L), FAKE, 2, FAKE, FAKE, 0, FAKE, None, None, FAKE, 64, None) == 7
