@@ -128,7 +128,7 @@ dv_status check_pred(const dv_predictor* P) {
 // Workspace layout (sized with the largest tiling any device can pick).
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t z, s_mlp, s_head, idx, heads, qkv, apart, o, h1, u, part, tk_mlp, tk_head, total;
+  size_t z, s_mlp, s_head, idx, heads, qkv, apart, o, h1, u, part, tk_mlp, tk_head, kpart, total;
   // batched path (B >= 2): union bitmaps and lists, fp16 operands
   size_t ubits, hbits, ulist, uhlist, counts, xh, xl, zh, zl, cu, co;
   int max_u, max_uh;
@@ -172,6 +172,7 @@ Layout layout_of(const dv_dims* d, int B, int k, int kh) {
     L.zl = take(2 * Bz * (d->rank_mlp + d->rank_head));
     L.cu = take(2 * Bz * (size_t)L.max_u);
     L.co = take(2 * Bz * (size_t)L.max_uh * d->head_dim);
+    L.kpart = take(4 * (size_t)dv::kRowsMaxSplit * Bz * dv::kRowsSplitMaxRows);
   }
   L.total = off;
   return L;
@@ -249,8 +250,9 @@ dv_status run_predict_stage2(const dv_dims* d, const dv_predictor* P, int B, flo
 bool batched(const dv_dims* d, int B) { return B >= DV_BATCH_MIN && B <= dv::kBatchMax && is_f16(d); }
 
 dv::GemmRowsArgs rows_args(const void* W, long long ld, int dlen, const int32_t* sel, const int* nsel, int G,
-                           int n_groups, int B, const _Float16* X, long long ldx) {
+                           int n_groups, int B, const _Float16* X, long long ldx, float* kpart) {
   dv::GemmRowsArgs g{};
+  g.kpart = kpart; g.kld = dv::kRowsSplitMaxRows;
   g.W = W; g.ld = ld; g.d = dlen; g.sel = sel; g.n_groups_sel = nsel; g.G = G; g.n_groups = n_groups; g.B = B;
   g.X = X; g.ldx = ldx;
   return g;
@@ -267,16 +269,16 @@ dv_status run_predict_batched(const dv_dims* d, const dv_predictor* P, const flo
   _Float16* zh = at<_Float16>(ws, L.zh);
   _Float16* zl = at<_Float16>(ws, L.zl);
   DV_HIP(dv::launch_rows_norm_f16(x, D, nullptr, D, 0.f, B, xh, xl, D, st));
-  dv::GemmRowsArgs a = rows_args(P->p1_mlp, D, D, nullptr, nullptr, 1, rm, B, xh, D);
+  dv::GemmRowsArgs a = rows_args(P->p1_mlp, D, D, nullptr, nullptr, 1, rm, B, xh, D, at<float>(ws, L.kpart));
   a.X_lo = xl; a.mode = dv::kGemmOutF16; a.outh = zh; a.outh_lo = zl; a.ldo = rm + rh;
   DV_HIP(dv::launch_gemm_rows(a, rm, cus, st));
-  a = rows_args(P->p1_head, D, D, nullptr, nullptr, 1, rh, B, xh, D);
+  a = rows_args(P->p1_head, D, D, nullptr, nullptr, 1, rh, B, xh, D, at<float>(ws, L.kpart));
   a.X_lo = xl; a.mode = dv::kGemmOutF16; a.outh = zh + rm; a.outh_lo = zl + rm; a.ldo = rm + rh;
   DV_HIP(dv::launch_gemm_rows(a, rh, cus, st));
-  a = rows_args(P->p2_mlp, rm, rm, nullptr, nullptr, 1, d->d_ffn, B, zh, rm + rh);
+  a = rows_args(P->p2_mlp, rm, rm, nullptr, nullptr, 1, d->d_ffn, B, zh, rm + rh, at<float>(ws, L.kpart));
   a.X_lo = zl; a.mode = dv::kGemmOutF32; a.outf = s_mlp; a.ldo = d->d_ffn;
   DV_HIP(dv::launch_gemm_rows(a, d->d_ffn, cus, st));
-  a = rows_args(P->p2_head, rh, rh, nullptr, nullptr, 1, d->n_heads, B, zh + rm, rm + rh);
+  a = rows_args(P->p2_head, rh, rh, nullptr, nullptr, 1, d->n_heads, B, zh + rm, rm + rh, at<float>(ws, L.kpart));
   a.X_lo = zl + rm; a.mode = dv::kGemmOutF32; a.outf = s_head; a.ldo = d->n_heads;
   DV_HIP(dv::launch_gemm_rows(a, d->n_heads, cus, st));
   return DV_OK;
@@ -427,7 +429,8 @@ dv_status run_attn_batched(const dv_dims* d, const dv_layer* Lw, const float* x,
     if (!union_done) DV_TRY(run_union(d, B, nullptr, 0, heads, kh, L, ws, st));
     _Float16* xh = at<_Float16>(ws, L.xh);
     DV_HIP(dv::launch_rows_norm_f16(x, D, norm_g, D, 1e-5f, B, xh, nullptr, D, st));
-    dv::GemmRowsArgs q = rows_args(Lw->wqkv, D, D, at<int32_t>(ws, L.uhlist), counts + 1, 3 * dh, H, B, xh, D);
+    dv::GemmRowsArgs q = rows_args(Lw->wqkv, D, D, at<int32_t>(ws, L.uhlist), counts + 1, 3 * dh, H, B, xh, D,
+                                   at<float>(ws, L.kpart));
     q.bias = Lw->bqkv; q.rowbits = at<unsigned>(ws, L.hbits); q.bits_words = hw;
     q.mode = dv::kGemmOutQkv; q.outf = qkv; q.kh = kh;
     DV_HIP(dv::launch_gemm_rows(q, L.max_uh * 3 * dh, cus, st));
@@ -482,7 +485,8 @@ dv_status run_mlp_batched(const dv_dims* d, const dv_layer* Lw, const float* x, 
   _Float16* xh = at<_Float16>(ws, L.xh);
   DV_HIP(dv::launch_rows_norm_f16(x, D, norm_g, D, 1e-5f, B, xh, nullptr, D, st));
   _Float16* cu = at<_Float16>(ws, L.cu);
-  dv::GemmRowsArgs a = rows_args(Lw->w1t, D, D, at<int32_t>(ws, L.ulist), counts, 1, F, B, xh, D);
+  dv::GemmRowsArgs a = rows_args(Lw->w1t, D, D, at<int32_t>(ws, L.ulist), counts, 1, F, B, xh, D,
+                                 at<float>(ws, L.kpart));
   a.bias = Lw->b1; a.relu = 1; a.rowbits = at<unsigned>(ws, L.ubits); a.bits_words = (F + 31) / 32;
   a.mode = dv::kGemmOutF16; a.outh = cu; a.ldo = L.max_u;
   DV_HIP(dv::launch_gemm_rows(a, L.max_u, cus, st));

@@ -134,7 +134,7 @@ hipError_t launch_topk(const TopkArgs& a, int B, hipStream_t s);
 // ---------------------------------------------------------------------------
 constexpr int kUnionMaxN = 65536;    // groups (neurons or heads) per problem
 constexpr int kBatchMax = 32;        // rows per batched launch
-constexpr int kBatchMaxRG = 16;      // row groups of the down-projection
+constexpr int kBatchMaxRG = 32;      // row groups of the down-projection
 struct UnionProb {
   const int32_t* idx;       // [B][idx_bstride]: the row's k selected groups (ascending)
   long long idx_bstride;
@@ -178,7 +178,12 @@ struct GemmRowsArgs {                // out[b][i] = act(W[row_i] . X[b] + bias[r
   float* outf;
   long long ldo;
   int kh;                            // slots per row (kGemmOutQkv)
+  float* kpart;                      // nullable: [kRowsMaxSplit][B][kld] partial sums when K is split over blocks
+  long long kld;
+  int ksplit;                        // set by the launcher
 };
+constexpr int kRowsMaxSplit = 16;       // K slices of a short up-projection
+constexpr int kRowsSplitMaxRows = 4096; // only launches of at most this many rows split K
 hipError_t launch_gemm_rows(const GemmRowsArgs& a, int max_rows, int cus, hipStream_t s);
 
 struct GemmColsArgs {                // partial[b][rg][c] = sum_k C[b][k] W[row_k][c], MFMA

@@ -15,10 +15,10 @@
 //    is taken twice (W . X_hi + W . X_lo): the fp16 weights are exact, so the result then
 //    carries fp32-like activation precision (used for the predictor's scores).
 //  * gemm_cols (down-projection, Wo and W2): partial[b][rg][c] = sum over the rows of row
-//    group rg of C[b][k] * W[row_k][c]. The weight tile (32 rows x 128 columns) is staged
-//    in LDS transposed so each lane's B fragment (8 consecutive k at one column) is one
-//    16-byte LDS read. The row groups are summed by the ordered reduce kernel of the
-//    gather-axpy.
+//    group rg of C[b][k] * W[row_k][c]. Weight rows are read in 512-byte strips, transposed
+//    8 x 8 in registers and staged in LDS so each lane's B fragment (8 consecutive k at one
+//    column) is one 16-byte LDS read. The row groups are summed by the ordered reduce kernel
+//    of the gather-axpy.
 // Every sum has a fixed order: results are bitwise reproducible.
 #include <algorithm>
 
@@ -170,6 +170,32 @@ __global__ __launch_bounds__(kNormBlock) void rows_norm_f16_kernel(const float* 
 // ---------------------------------------------------------------------------
 constexpr int kGemmBlock = 256;   // 4 waves (gemm_cols)
 
+// Epilogue of one output (gathered row i, batch row b): bias, ReLU, the row's own mask, and
+// the store in the launch's output mode.
+__device__ __forceinline__ void rows_store(const GemmRowsArgs& a, int i, int b, float acc) {
+  const int g = i / a.G;
+  const int wi = i - g * a.G;
+  const int grp = a.sel ? a.sel[g] : g;
+  const bool gv = (unsigned)grp < (unsigned)a.n_groups;
+  const long long row = gv ? (long long)grp * a.G + wi : 0;
+  const float bias = (gv && a.bias) ? a.bias[row] : 0.f;
+  const unsigned* rb = a.rowbits ? a.rowbits + (long long)b * a.bits_words : nullptr;
+  const bool on = gv && (rb == nullptr || bit_of(rb, grp));
+  float v = acc + bias;
+  if (a.relu) v = fmaxf(v, 0.f);
+  if (a.mode == kGemmOutF16) {
+    const float vv = on ? v : 0.f;
+    const _Float16 hi = static_cast<_Float16>(vv);
+    a.outh[(long long)b * a.ldo + i] = hi;
+    if (a.outh_lo) a.outh_lo[(long long)b * a.ldo + i] = static_cast<_Float16>(vv - static_cast<float>(hi));
+  } else if (a.mode == kGemmOutF32) {
+    a.outf[(long long)b * a.ldo + i] = on ? v : 0.f;
+  } else if (on && rb != nullptr) {   // q/k/v into the row's own slot order
+    const int slot = rank_below(rb, grp);
+    a.outf[((long long)b * a.kh + slot) * a.G + wi] = v;
+  }
+}
+
 // A block of KW waves owns MT tiles of 16 gathered rows; its waves split K into KW
 // contiguous ranges, each keeping two batches of UK K-steps of loads in flight. The MT row
 // tiles of a wave share their activation (B) fragments. Partial tiles are summed through
@@ -215,9 +241,12 @@ __global__ __launch_bounds__(KW * kWave) void gemm_rows_kernel(GemmRowsArgs a) {
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-  const int nk = (a.d + 31) / 32;
-  const int per = (nk + KW - 1) / KW;
-  const int kbeg = min(nk, wv * per), kend = min(nk, kbeg + per);
+  // K steps of this block's slice (grid.y slices when K is split over blocks), then of this wave
+  const int nk_all = (a.d + 31) / 32;
+  const int sb = (int)((long long)nk_all * blockIdx.y / gridDim.y);
+  const int se = (int)((long long)nk_all * (blockIdx.y + 1) / gridDim.y);
+  const int per = (se - sb + KW - 1) / KW;
+  const int kbeg = min(se, sb + wv * per), kend = min(se, kbeg + per);
 
   struct Batch {
     u32x4 av[UK][MT];
@@ -299,63 +328,62 @@ __global__ __launch_bounds__(KW * kWave) void gemm_rows_kernel(GemmRowsArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int i = r0 + 16 * mt + 4 * lg + e;
       if (i >= nrows) continue;
-      const int g = i / a.G;
-      const int wi = i - g * a.G;
-      const int grp = a.sel ? a.sel[g] : g;
-      const bool gv = (unsigned)grp < (unsigned)a.n_groups;
-      const long long row = gv ? (long long)grp * a.G + wi : 0;
-      const float bias = (gv && a.bias) ? a.bias[row] : 0.f;
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const int b = nt * 16 + lr;
         if (b >= a.B) continue;
-        const unsigned* rb = a.rowbits ? a.rowbits + (long long)b * a.bits_words : nullptr;
-        const bool on = gv && (rb == nullptr || bit_of(rb, grp));
-        float v = acc[mt][nt][e] + bias;
-        if (a.relu) v = fmaxf(v, 0.f);
-        if (a.mode == kGemmOutF16) {
-          const float vv = on ? v : 0.f;
-          const _Float16 hi = static_cast<_Float16>(vv);
-          a.outh[(long long)b * a.ldo + i] = hi;
-          if (a.outh_lo) a.outh_lo[(long long)b * a.ldo + i] = static_cast<_Float16>(vv - static_cast<float>(hi));
-        } else if (a.mode == kGemmOutF32) {
-          a.outf[(long long)b * a.ldo + i] = on ? v : 0.f;
-        } else if (on && rb != nullptr) {   // q/k/v into the row's own slot order
-          const int slot = rank_below(rb, grp);
-          a.outf[((long long)b * a.kh + slot) * a.G + wi] = v;
-        }
+        if (gridDim.y > 1) a.kpart[((long long)blockIdx.y * a.B + b) * a.kld + i] = acc[mt][nt][e];
+        else rows_store(a, i, b, acc[mt][nt][e]);
       }
     }
+}
+
+// Sum of the K slices of a split up-projection, in slice order, then the epilogue.
+__global__ void gemm_rows_finish_kernel(GemmRowsArgs a) {
+  const int nrows = (a.n_groups_sel ? *a.n_groups_sel : a.n_groups) * a.G;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.y;
+  if (i >= nrows) return;
+  float v = 0.f;
+  for (int q = 0; q < a.ksplit; ++q) v += a.kpart[((long long)q * a.B + b) * a.kld + i];
+  rows_store(a, i, b, v);
 }
 
 // ---------------------------------------------------------------------------
 // gemm_cols: down-projection over gathered rows, row groups -> partials
 // ---------------------------------------------------------------------------
-constexpr int kColsNT = 128;        // output columns per block (8 MFMA column tiles)
-constexpr int kColsKT = 64;         // gathered rows per LDS tile
-constexpr int kColsPad = 8;         // halfs of padding per transposed column
-constexpr int kColsLd = kColsKT + kColsPad;
-constexpr int kColsLoads = kColsKT * kColsNT * 2 / 16 / kGemmBlock;   // 16-byte loads per thread per tile
+#ifndef DV_COLS_CW
+#define DV_COLS_CW 256   // output columns per block: 512-byte strips of every weight row
+#endif
 
-// The next tile's weight rows are loaded into registers while the current tile is
-// transposed into LDS and consumed, so one tile is always in flight behind the MFMAs.
-template <int MT>
+// A tile is KT gathered rows x CW columns (32 KB). Each thread loads the same 8 columns of 8
+// consecutive rows (for a fixed row, a wave reads CW/8*16 contiguous bytes per row), transposes
+// that 8 x 8 block in registers and writes each column's 8 rows as one 16-byte LDS store: the
+// B fragment of the MFMA (8 consecutive k at one column) is then one 16-byte LDS read. The next
+// tile's rows are in flight while the current one is transposed and consumed.
+template <int MT, int CW>
 __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
-  __shared__ __attribute__((aligned(16))) half_t s_w[kColsNT * kColsLd];
+  constexpr int TPC = CW / 8;             // threads across the tile's columns
+  constexpr int RGP = kGemmBlock / TPC;   // 8-row groups per tile
+  constexpr int KT = 8 * RGP;             // rows per tile
+  constexpr int LDK = KT + 8;             // halfs per transposed column (padded)
+  constexpr int CTW = CW / 16 / (kGemmBlock / kWave);   // 16-column MFMA tiles per wave
+  constexpr int KS = KT / 32;             // MFMA k-steps per tile
+  static_assert(KT % 32 == 0 && CTW >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) half_t s_w[CW * LDK];
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int lr = lane % 16, lg = lane / 16;
-  const int c0 = blockIdx.x * kColsNT;
+  const int tc = tid % TPC, trg = tid / TPC;
+  const int c0 = blockIdx.x * CW;
   const int rg = blockIdx.y;
   const int K = *a.n_groups_sel * a.G;
   int rpg = (K + a.RG - 1) / a.RG;
-  rpg = (rpg + kColsKT - 1) / kColsKT * kColsKT;
+  rpg = (rpg + KT - 1) / KT * KT;
   const int kb0 = min(K, rg * rpg);
   const int kend = min(K, kb0 + rpg);
   const half_t* W = reinterpret_cast<const half_t*>(a.W);
-  // tile loader: thread -> rows tr + 16*h (h < kColsLoads), 8 columns at c0 + 8*tc
-  const int tr = tid / 16, tc = tid % 16;
   const int col = c0 + 8 * tc;
-  const bool colv = col < a.d;
+  const bool colv = col < a.d;   // d is a multiple of 8: a chunk is wholly in or out
   auto row_of = [&](int k) -> long long {
     if (k >= kend) return -1;
     const int g = k / a.G;
@@ -365,21 +393,16 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
   };
   auto load_tile = [&](u32x4* wt, int kb) {
 #pragma unroll
-    for (int h = 0; h < kColsLoads; ++h) {
-      const long long r = row_of(kb + tr + 16 * h);
-      wt[h] = (r >= 0 && colv) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + r * a.ld + col))
+    for (int q = 0; q < 8; ++q) {
+      const long long r = row_of(kb + 8 * trg + q);
+      wt[q] = (r >= 0 && colv) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + r * a.ld + col))
                                : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  f4v acc[2][MT];
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[q][mt] = f4v{0.f, 0.f, 0.f, 0.f};
-  // A fragments of a tile: coefficients C[b][kb + 32*ks + 8*lg .. +8] of batch rows 16*mt + lr
+  // A fragments: coefficients C[b][kb + 32*ks + 8*lg .. +8] of batch rows 16*mt + lr
   auto load_coef = [&](h8v (*cf)[MT], int kb) {
 #pragma unroll
-    for (int ks = 0; ks < kColsKT / 32; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int k = kb + 32 * ks + 8 * lg;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -398,56 +421,59 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
       }
     }
   };
-  u32x4 cur[kColsLoads], nxt[kColsLoads];
-  h8v ccur[kColsKT / 32][MT], cnxt[kColsKT / 32][MT];
+  f4v acc[CTW][MT];
+#pragma unroll
+  for (int i = 0; i < CTW; ++i)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[i][mt] = f4v{0.f, 0.f, 0.f, 0.f};
+  u32x4 cur[8], nxt[8];
+  h8v ccur[KS][MT], cnxt[KS][MT];
   if (kb0 < kend) {
     load_tile(cur, kb0);
     load_coef(ccur, kb0);
   }
-  for (int kb = kb0; kb < kend; kb += kColsKT) {   // block-uniform
-    if (kb + kColsKT < kend) {
-      load_tile(nxt, kb + kColsKT);
-      load_coef(cnxt, kb + kColsKT);
+  for (int kb = kb0; kb < kend; kb += KT) {   // block-uniform
+    if (kb + KT < kend) {
+      load_tile(nxt, kb + KT);
+      load_coef(cnxt, kb + KT);
     }
+    h8v colv8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) colv8[j][q] = __builtin_bit_cast(h8v, cur[q])[j];
     __syncthreads();   // the previous tile's readers are done
 #pragma unroll
-    for (int h = 0; h < kColsLoads; ++h) {
-      const h8v v = __builtin_bit_cast(h8v, cur[h]);
-      const int kk = tr + 16 * h;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s_w[(8 * tc + e) * kColsLd + kk] = v[e];
-    }
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<h8v*>(&s_w[(8 * tc + j) * LDK + 8 * trg]) = colv8[j];
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < kColsKT / 32; ++ks) {
-      // wave wv: column tiles 2*wv and 2*wv + 1
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int cl = (2 * wv + q) * 16 + lr;
-        const h8v bf = *reinterpret_cast<const h8v*>(&s_w[cl * kColsLd + 32 * ks + 8 * lg]);
+      for (int i = 0; i < CTW; ++i) {
+        const int cl = (wv * CTW + i) * 16 + lr;
+        const h8v bf = *reinterpret_cast<const h8v*>(&s_w[cl * LDK + 32 * ks + 8 * lg]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          acc[q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ccur[ks][mt], bf, acc[q][mt], 0, 0, 0);
+          acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ccur[ks][mt], bf, acc[i][mt], 0, 0, 0);
       }
-    }
 #pragma unroll
-    for (int h = 0; h < kColsLoads; ++h) cur[h] = nxt[h];
+    for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
 #pragma unroll
-    for (int ks = 0; ks < kColsKT / 32; ++ks)
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) ccur[ks][mt] = cnxt[ks][mt];
   }
   // D layout: lane holds output column lr of its tile, batch rows 16*mt + 4*lg + e
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c = c0 + (2 * wv + q) * 16 + lr;
+  for (int i = 0; i < CTW; ++i) {
+    const int c = c0 + (wv * CTW + i) * 16 + lr;
     if (c >= a.d) continue;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int b = 16 * mt + 4 * lg + e;
-        if (b < a.B) a.partial[((long long)b * a.RG + rg) * a.d + c] = acc[q][mt][e];
+        if (b < a.B) a.partial[((long long)b * a.RG + rg) * a.d + c] = acc[i][mt][e];
       }
   }
 }
@@ -505,10 +531,39 @@ static void launch_rows_cfg(const GemmRowsArgs& a, int max_rows, int cus, hipStr
   }
 }
 
-hipError_t launch_gemm_rows(const GemmRowsArgs& a, int max_rows, int cus, hipStream_t s) {
+// A short launch (fewer row tiles than CUs) splits K over blocks: slice q of every tile
+// writes its partial sums, and the finishing kernel adds the slices in order.
+template <int NT, bool SPLIT>
+static void launch_rows_ksplit(const GemmRowsArgs& a, int max_rows, int ks, hipStream_t s) {
+  const int tiles = (max_rows + 15) / 16;
+  hipLaunchKernelGGL((gemm_rows_kernel<NT, SPLIT, 1, 4>), dim3(tiles, ks), dim3(4 * kWave), 0, s, a);
+}
+
+hipError_t launch_gemm_rows(const GemmRowsArgs& a_in, int max_rows, int cus, hipStream_t s) {
+  GemmRowsArgs a = a_in;
   if (a.d % 8 != 0 || a.B < 1 || a.B > kBatchMax || max_rows < 0) return hipErrorInvalidValue;   // tail K steps are guarded
   if (max_rows == 0) return hipSuccess;
   const bool split = a.X_lo != nullptr;
+  const int tiles = (max_rows + 15) / 16;
+  const int nk = (a.d + 31) / 32;
+  int ks = 1;
+  if (a.kpart != nullptr && max_rows <= kRowsSplitMaxRows && tiles < cus && a.kld >= max_rows)
+    ks = std::max(1, std::min({(2 * cus + tiles - 1) / tiles, nk / 8, kRowsMaxSplit}));
+  if (ks > 1) {
+    a.ksplit = ks;
+    if (a.B <= 16) {
+      if (split) launch_rows_ksplit<1, true>(a, max_rows, ks, s);
+      else launch_rows_ksplit<1, false>(a, max_rows, ks, s);
+    } else {
+      if (split) launch_rows_ksplit<2, true>(a, max_rows, ks, s);
+      else launch_rows_ksplit<2, false>(a, max_rows, ks, s);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_rows_finish_kernel, dim3((max_rows + 255) / 256, a.B), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  a.ksplit = 1;
   if (a.B <= 16) {
     if (split) launch_rows_cfg<1, true>(a, max_rows, cus, s);
     else launch_rows_cfg<1, false>(a, max_rows, cus, s);
@@ -520,9 +575,10 @@ hipError_t launch_gemm_rows(const GemmRowsArgs& a, int max_rows, int cus, hipStr
 }
 
 int gemm_cols_rg(int d, int max_rows, int B, int cus) {
-  const int ctiles = (d + kColsNT - 1) / kColsNT;
-  int rg = (4 * cus + ctiles - 1) / ctiles;               // about four blocks per CU
-  const int cap = max(1, max_rows / (2 * kColsKT));       // at least 2 tiles of rows per group
+  constexpr int KT = 8 * kGemmBlock / (DV_COLS_CW / 8);
+  const int ctiles = (d + DV_COLS_CW - 1) / DV_COLS_CW;
+  int rg = (3 * cus + ctiles - 1) / ctiles;               // about three blocks per CU
+  const int cap = max(1, max_rows / (2 * KT));            // at least 2 tiles of rows per group
   rg = min(rg, cap);
   rg = min(rg, kBatchMaxRG);
   while (rg > 1 && (long long)rg * B > 1024) --rg;        // bounds the partial buffer
@@ -531,9 +587,9 @@ int gemm_cols_rg(int d, int max_rows, int B, int cus) {
 
 hipError_t launch_gemm_cols(const GemmColsArgs& a, hipStream_t s) {
   if (a.d % 8 != 0 || a.B < 1 || a.B > kBatchMax || a.RG < 1 || a.RG > kBatchMaxRG) return hipErrorInvalidValue;
-  const dim3 grid((a.d + kColsNT - 1) / kColsNT, a.RG);
-  if (a.B <= 16) hipLaunchKernelGGL((gemm_cols_kernel<1>), grid, dim3(kGemmBlock), 0, s, a);
-  else hipLaunchKernelGGL((gemm_cols_kernel<2>), grid, dim3(kGemmBlock), 0, s, a);
+  const dim3 grid((a.d + DV_COLS_CW - 1) / DV_COLS_CW, a.RG);
+  if (a.B <= 16) hipLaunchKernelGGL((gemm_cols_kernel<1, DV_COLS_CW>), grid, dim3(kGemmBlock), 0, s, a);
+  else hipLaunchKernelGGL((gemm_cols_kernel<2, DV_COLS_CW>), grid, dim3(kGemmBlock), 0, s, a);
   return hipGetLastError();
 }
 
