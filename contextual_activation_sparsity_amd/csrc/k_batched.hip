@@ -338,6 +338,101 @@ __global__ __launch_bounds__(KW * kWave) void gemm_rows_kernel(GemmRowsArgs a) {
     }
 }
 
+// Long up-projections: a block of 4 waves owns 64 gathered rows (a 16-row MFMA tile per wave)
+// over the whole of K, staged through LDS in chunks of kRowsKC: one load instruction of a
+// wave covers 2 rows x 512 contiguous bytes, and the activation rows (and their remainders)
+// are staged once per block instead of once per wave. The next chunk's loads are in flight
+// while the MFMAs consume the current one. No cross-wave sum: each wave owns its rows.
+constexpr int kRowsKC = 256;
+constexpr int kRowsLdk = kRowsKC + 8;
+template <int NT, bool SPLIT>
+__global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
+  constexpr int NX = NT * 16;                   // staged activation rows
+  constexpr int XL = SPLIT ? 2 : 1;
+  constexpr int XLD = NX * kRowsKC / 8 / 256;   // 16-byte activation loads per thread per array
+  __shared__ __attribute__((aligned(16))) half_t s_w[64 * kRowsLdk];
+  __shared__ __attribute__((aligned(16))) _Float16 s_x[XL][NX * kRowsLdk];
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int lr = lane % 16, lg = lane / 16;
+  const int nrows = (a.n_groups_sel ? *a.n_groups_sel : a.n_groups) * a.G;
+  const int r0 = blockIdx.x * 64;
+  if (r0 >= nrows) return;   // block-uniform
+  const half_t* W = reinterpret_cast<const half_t*>(a.W);
+  // loader: thread -> rows lrow + 8*q (q < 8), 8 halfs at k = kk
+  const int lrow = tid / 32, kk = 8 * (tid % 32);
+  const half_t* wp[8];
+  bool wok[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int i = r0 + lrow + 8 * q;
+    long long wrow = -1;
+    if (i < nrows) {
+      const int g = i / a.G;
+      const int grp = a.sel ? a.sel[g] : g;
+      if ((unsigned)grp < (unsigned)a.n_groups) wrow = (long long)grp * a.G + (i - g * a.G);
+    }
+    wok[q] = wrow >= 0;
+    wp[q] = W + (wrow >= 0 ? wrow : 0) * a.ld + kk;
+  }
+  u32x4 wreg[8];
+  h8v xreg[XL][XLD];
+  auto load = [&](int k0) {
+    const bool kok = k0 + kk < a.d;   // d is a multiple of 8: a chunk is wholly in or out
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      wreg[q] = (kok && wok[q]) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[q] + k0))
+                                : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int p = 0; p < XLD; ++p) {
+      const int b = lrow + 8 * p;
+      const bool ok = kok && b < a.B;
+      xreg[0][p] = ok ? *reinterpret_cast<const h8v*>(a.X + (long long)b * a.ldx + k0 + kk) : h8v{0, 0, 0, 0, 0, 0, 0, 0};
+      if constexpr (SPLIT)
+        xreg[1][p] = ok ? *reinterpret_cast<const h8v*>(a.X_lo + (long long)b * a.ldx + k0 + kk)
+                        : h8v{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  };
+  f4v acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
+  load(0);
+  for (int k0 = 0; k0 < a.d; k0 += kRowsKC) {   // block-uniform
+    __syncthreads();   // the previous chunk's readers are done
+#pragma unroll
+    for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4*>(&s_w[(lrow + 8 * q) * kRowsLdk + kk]) = wreg[q];
+#pragma unroll
+    for (int x = 0; x < XL; ++x)
+#pragma unroll
+      for (int p = 0; p < XLD; ++p) *reinterpret_cast<h8v*>(&s_x[x][(lrow + 8 * p) * kRowsLdk + kk]) = xreg[x][p];
+    __syncthreads();
+    if (k0 + kRowsKC < a.d) load(k0 + kRowsKC);
+    const int nks = min(kRowsKC, a.d - k0 + 31) / 32;   // k-steps holding data (the rest are zero)
+    for (int ks = 0; ks < nks; ++ks) {
+      const h8v af = *reinterpret_cast<const h8v*>(&s_w[(16 * wv + lr) * kRowsLdk + 32 * ks + 8 * lg]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const h8v bf = *reinterpret_cast<const h8v*>(&s_x[0][(16 * nt + lr) * kRowsLdk + 32 * ks + 8 * lg]);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[nt], 0, 0, 0);
+        if constexpr (SPLIT) {
+          const h8v bl = *reinterpret_cast<const h8v*>(&s_x[XL - 1][(16 * nt + lr) * kRowsLdk + 32 * ks + 8 * lg]);
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bl, acc[nt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // D layout: lane holds batch row 16*nt + lr, gathered rows r0 + 16*wv + 4*lg + e
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = r0 + 16 * wv + 4 * lg + e;
+    if (i >= nrows) continue;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int b = nt * 16 + lr;
+      if (b < a.B) rows_store(a, i, b, acc[nt][e]);
+    }
+  }
+}
+
 // Sum of the K slices of a split up-projection, in slice order, then the epilogue.
 __global__ void gemm_rows_finish_kernel(GemmRowsArgs a) {
   const int nrows = (a.n_groups_sel ? *a.n_groups_sel : a.n_groups) * a.G;
@@ -371,6 +466,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
   constexpr int KS = KT / 32;             // MFMA k-steps per tile
   static_assert(KT % 32 == 0 && CTW >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) half_t s_w[CW * LDK];
+  __shared__ __attribute__((aligned(16))) _Float16 s_c[MT * 16 * LDK];   // coefficients [b][k] of the tile
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int lr = lane % 16, lg = lane / 16;
   const int tc = tid % TPC, trg = tid / TPC;
@@ -384,40 +480,40 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
   const half_t* W = reinterpret_cast<const half_t*>(a.W);
   const int col = c0 + 8 * tc;
   const bool colv = col < a.d;   // d is a multiple of 8: a chunk is wholly in or out
-  auto row_of = [&](int k) -> long long {
+  auto row_of = [&](int k) -> int {   // weight row of union position k, -1 past the group
     if (k >= kend) return -1;
     const int g = k / a.G;
     const int grp = a.sel[g];
     if ((unsigned)grp >= (unsigned)a.n_groups) return -1;
-    return (long long)grp * a.G + (k - g * a.G);
+    return grp * a.G + (k - g * a.G);
   };
-  auto load_tile = [&](u32x4* wt, int kb) {
+  // Row numbers of a tile come from the union list; they are fetched two tiles ahead, before
+  // the weight loads of the tile in between, so waiting for them never waits for weights.
+  auto rows_for = [&](int* r, int kb) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const long long r = row_of(kb + 8 * trg + q);
-      wt[q] = (r >= 0 && colv) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + r * a.ld + col))
-                               : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int q = 0; q < 8; ++q) r[q] = row_of(kb + 8 * trg + q);
   };
-  // A fragments: coefficients C[b][kb + 32*ks + 8*lg .. +8] of batch rows 16*mt + lr
-  auto load_coef = [&](h8v (*cf)[MT], int kb) {
+  auto load_tile = [&](u32x4* wt, const int* r) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int k = kb + 32 * ks + 8 * lg;
+    for (int q = 0; q < 8; ++q)
+      wt[q] = (r[q] >= 0 && colv)
+                  ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(W + (long long)r[q] * a.ld + col))
+                  : u32x4{0u, 0u, 0u, 0u};
+  };
+  // Coefficient tile C[b][kb .. kb + KT) for the MT*16 batch rows, staged in LDS with the
+  // weights: thread -> batch row tid / (KT/8), 8 consecutive k at 8 * (tid % (KT/8)).
+  constexpr int CPR = KT / 8;   // 16-byte chunks per coefficient row
+  const int cb = tid / CPR, ck = 8 * (tid % CPR);
+  auto load_coef = [&](h8v& cf, int kb) {
+    const int k = kb + ck;
+    cf = h8v{0, 0, 0, 0, 0, 0, 0, 0};
+    if (cb < MT * 16 && cb < a.B && k < kend) {
+      const _Float16* cp = a.C + (long long)cb * a.ldc + k;
+      if (k + 8 <= kend) {
+        cf = *reinterpret_cast<const h8v*>(cp);
+      } else {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int b = 16 * mt + lr;
-        if (b < a.B && k < kend) {
-          const _Float16* cp = a.C + (long long)b * a.ldc + k;
-          if (k + 8 <= kend) {
-            cf[ks][mt] = *reinterpret_cast<const h8v*>(cp);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cf[ks][mt][e] = (k + e < kend) ? cp[e] : static_cast<_Float16>(0.f);
-          }
-        } else {
-          cf[ks][mt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+        for (int e = 0; e < 8; ++e) cf[e] = (k + e < kend) ? cp[e] : static_cast<_Float16>(0.f);
       }
     }
   };
@@ -427,14 +523,18 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[i][mt] = f4v{0.f, 0.f, 0.f, 0.f};
   u32x4 cur[8], nxt[8];
-  h8v ccur[KS][MT], cnxt[KS][MT];
+  h8v ccur, cnxt;
+  int rn[8], rnn[8];
   if (kb0 < kend) {
-    load_tile(cur, kb0);
+    rows_for(rn, kb0);
+    load_tile(cur, rn);
     load_coef(ccur, kb0);
+    rows_for(rn, kb0 + KT);
   }
   for (int kb = kb0; kb < kend; kb += KT) {   // block-uniform
+    rows_for(rnn, kb + 2 * KT);   // no loads past the group's end (row_of returns -1 there)
     if (kb + KT < kend) {
-      load_tile(nxt, kb + KT);
+      load_tile(nxt, rn);
       load_coef(cnxt, kb + KT);
     }
     h8v colv8[8];
@@ -445,6 +545,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
     __syncthreads();   // the previous tile's readers are done
 #pragma unroll
     for (int j = 0; j < 8; ++j) *reinterpret_cast<h8v*>(&s_w[(8 * tc + j) * LDK + 8 * trg]) = colv8[j];
+    if (cb < MT * 16) *reinterpret_cast<h8v*>(&s_c[cb * LDK + ck]) = ccur;
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -453,15 +554,17 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
         const int cl = (wv * CTW + i) * 16 + lr;
         const h8v bf = *reinterpret_cast<const h8v*>(&s_w[cl * LDK + 32 * ks + 8 * lg]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ccur[ks][mt], bf, acc[i][mt], 0, 0, 0);
+        for (int mt = 0; mt < MT; ++mt) {
+          const h8v af = *reinterpret_cast<const h8v*>(&s_c[(16 * mt + lr) * LDK + 32 * ks + 8 * lg]);
+          acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[i][mt], 0, 0, 0);
+        }
       }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) ccur[ks][mt] = cnxt[ks][mt];
+    for (int q = 0; q < 8; ++q) {
+      cur[q] = nxt[q];
+      rn[q] = rnn[q];
+    }
+    ccur = cnxt;
   }
   // D layout: lane holds output column lr of its tile, batch rows 16*mt + 4*lg + e
 #pragma unroll
@@ -531,6 +634,10 @@ static void launch_rows_cfg(const GemmRowsArgs& a, int max_rows, int cus, hipStr
   }
 }
 
+#ifndef DV_ROWS_LDS
+#define DV_ROWS_LDS 1
+#endif
+
 // A short launch (fewer row tiles than CUs) splits K over blocks: slice q of every tile
 // writes its partial sums, and the finishing kernel adds the slices in order.
 template <int NT, bool SPLIT>
@@ -564,6 +671,19 @@ hipError_t launch_gemm_rows(const GemmRowsArgs& a_in, int max_rows, int cus, hip
     return hipGetLastError();
   }
   a.ksplit = 1;
+#if DV_ROWS_LDS
+  if (max_rows > kRowsSplitMaxRows || ks == 1) {
+    const dim3 grid((max_rows + 63) / 64);
+    if (a.B <= 16) {
+      if (split) hipLaunchKernelGGL((gemm_rows_lds_kernel<1, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gemm_rows_lds_kernel<1, false>), grid, dim3(256), 0, s, a);
+    } else {
+      if (split) hipLaunchKernelGGL((gemm_rows_lds_kernel<2, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((gemm_rows_lds_kernel<2, false>), grid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+  }
+#endif
   if (a.B <= 16) {
     if (split) launch_rows_cfg<1, true>(a, max_rows, cus, s);
     else launch_rows_cfg<1, false>(a, max_rows, cus, s);
