@@ -182,7 +182,7 @@ struct GemmRowsArgs {                // out[b][i] = act(W[row_i] . X[b] + bias[r
   long long kld;
   int ksplit;                        // set by the launcher
 };
-constexpr int kRowsMaxSplit = 16;       // K slices of a short up-projection
+constexpr int kRowsMaxSplit = 32;       // K slices of a short up-projection
 constexpr int kRowsSplitMaxRows = 4096; // only launches of at most this many rows split K
 hipError_t launch_gemm_rows(const GemmRowsArgs& a, int max_rows, int cus, hipStream_t s);
 

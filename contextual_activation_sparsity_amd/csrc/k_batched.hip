@@ -9,11 +9,12 @@
 //    or heads), their OR, and the OR as an ascending list with its length in device memory.
 //  * rows_norm_f16: RMSNorm of each row, rounded to fp16 (the MFMA operand type).
 //  * gemm_rows (up-projection, q/k/v and W1; both predictor factors): out[b][i] =
-//    act(W[row_i] . X[b] + bias), masked per row. A wave owns 16 gathered rows; A fragments
-//    are 16-byte loads along a weight row, B fragments 16-byte loads along an activation
-//    row, fp32 accumulation with v_mfma_f32_16x16x32_f16. With a low part X_lo the product
-//    is taken twice (W . X_hi + W . X_lo): the fp16 weights are exact, so the result then
-//    carries fp32-like activation precision (used for the predictor's scores).
+//    act(W[row_i] . X[b] + bias), masked per row. A block stages 64 gathered weight rows and
+//    the B activation rows through LDS in K chunks (contiguous 512-byte row pieces per load
+//    instruction); a wave owns 16 rows, fp32 accumulation with v_mfma_f32_16x16x32_f16.
+//    With a low part X_lo the product is taken twice (W . X_hi + W . X_lo): the fp16 weights
+//    are exact, so the result then carries fp32-like activation precision (used for the
+//    predictor's scores). Short launches split K over blocks and add the slices in order.
 //  * gemm_cols (down-projection, Wo and W2): partial[b][rg][c] = sum over the rows of row
 //    group rg of C[b][k] * W[row_k][c]. Weight rows are read in 512-byte strips, transposed
 //    8 x 8 in registers and staged in LDS so each lane's B fragment (8 consecutive k at one
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(kNormBlock) void rows_norm_f16_kernel(const float* 
 // ---------------------------------------------------------------------------
 // gemm_rows: up-projection over gathered rows
 // ---------------------------------------------------------------------------
-constexpr int kGemmBlock = 256;   // 4 waves (gemm_cols)
+constexpr int kGemmBlock = 256;   // 4 waves
 
 // Epilogue of one output (gathered row i, batch row b): bias, ReLU, the row's own mask, and
 // the store in the launch's output mode.
@@ -196,150 +197,10 @@ __device__ __forceinline__ void rows_store(const GemmRowsArgs& a, int i, int b, 
   }
 }
 
-// A block of KW waves owns MT tiles of 16 gathered rows; its waves split K into KW
-// contiguous ranges, each keeping two batches of UK K-steps of loads in flight. The MT row
-// tiles of a wave share their activation (B) fragments. Partial tiles are summed through
-// LDS in wave order (fixed, so deterministic).
-template <int NT, bool SPLIT, int MT, int KW>
-__global__ __launch_bounds__(KW * kWave) void gemm_rows_kernel(GemmRowsArgs a) {
-  constexpr int UK = MT >= 4 ? 2 : 4;
-  __shared__ float s_acc[KW][MT][NT][4][kWave];
-  const int lane = threadIdx.x % kWave;
-  const int wv = threadIdx.x / kWave;
-  const int nrows = (a.n_groups_sel ? *a.n_groups_sel : a.n_groups) * a.G;
-  const int r0 = blockIdx.x * 16 * MT;
-  if (r0 >= nrows) return;   // block-uniform: the whole block leaves before any barrier
-  const int lr = lane % 16, lg = lane / 16;
-  const half_t* W = reinterpret_cast<const half_t*>(a.W);
-  // A operands: weight row of lane row lr in each of the MT tiles
-  const half_t* wp[MT];
-  bool wok[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int ia = r0 + 16 * mt + lr;
-    long long wrow = -1;
-    if (ia < nrows) {
-      const int g = ia / a.G;
-      const int grp = a.sel ? a.sel[g] : g;
-      if ((unsigned)grp < (unsigned)a.n_groups) wrow = (long long)grp * a.G + (ia - g * a.G);
-    }
-    wok[mt] = wrow >= 0;
-    wp[mt] = W + (wrow >= 0 ? wrow : 0) * a.ld + 8 * lg;
-  }
-  const _Float16* xp[NT];
-  const _Float16* xq[NT];   // low parts (SPLIT)
-  bool xv[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int b = nt * 16 + lr;
-    xv[nt] = b < a.B;
-    xp[nt] = a.X + (long long)(xv[nt] ? b : 0) * a.ldx + 8 * lg;
-    xq[nt] = SPLIT ? a.X_lo + (long long)(xv[nt] ? b : 0) * a.ldx + 8 * lg : nullptr;
-  }
-  f4v acc[MT][NT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f4v{0.f, 0.f, 0.f, 0.f};
-  // K steps of this block's slice (grid.y slices when K is split over blocks), then of this wave
-  const int nk_all = (a.d + 31) / 32;
-  const int sb = (int)((long long)nk_all * blockIdx.y / gridDim.y);
-  const int se = (int)((long long)nk_all * (blockIdx.y + 1) / gridDim.y);
-  const int per = (se - sb + KW - 1) / KW;
-  const int kbeg = min(se, sb + wv * per), kend = min(se, kbeg + per);
-
-  struct Batch {
-    u32x4 av[UK][MT];
-    h8v bv[UK][NT];
-    h8v bl[SPLIT ? UK : 1][NT];
-  };
-  auto load = [&](Batch& q, int k0) {
-#pragma unroll
-    for (int u = 0; u < UK; ++u) {
-      const int ks = k0 + u;
-      const bool ok = ks < kend && ks * 32 + 8 * lg + 8 <= a.d;   // d is a multiple of 8
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        q.av[u][mt] = (ok && wok[mt]) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp[mt] + (long long)ks * 32))
-                                      : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (ok && xv[nt]) q.bv[u][nt] = *reinterpret_cast<const h8v*>(xp[nt] + (long long)ks * 32);
-        else q.bv[u][nt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
-        if constexpr (SPLIT) {
-          if (ok && xv[nt]) q.bl[u][nt] = *reinterpret_cast<const h8v*>(xq[nt] + (long long)ks * 32);
-          else q.bl[u][nt] = h8v{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-      }
-    }
-  };
-  auto mma = [&](const Batch& q) {
-#pragma unroll
-    for (int u = 0; u < UK; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const h8v ah = __builtin_bit_cast(h8v, q.av[u][mt]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, q.bv[u][nt], acc[mt][nt], 0, 0, 0);
-          if constexpr (SPLIT)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, q.bl[u][nt], acc[mt][nt], 0, 0, 0);
-        }
-      }
-  };
-  Batch q0, q1;
-  int k0 = kbeg;
-  if (k0 < kend) load(q0, k0);
-  while (k0 < kend) {   // per-wave trip count; no barriers inside
-    const int k1 = k0 + UK;
-    if (k1 < kend) load(q1, k1);
-    mma(q0);
-    k0 = k1;
-    if (k0 >= kend) break;
-    const int k2 = k0 + UK;
-    if (k2 < kend) load(q0, k2);
-    mma(q1);
-    k0 = k2;
-  }
-  // the KW K-ranges of each tile, summed in wave order by wave 0
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_acc[wv][mt][nt][e][lane] = acc[mt][nt][e];
-  __syncthreads();
-  if (wv != 0) return;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < KW; ++w) v += s_acc[w][mt][nt][e][lane];
-        acc[mt][nt][e] = v;
-      }
-  // D layout: lane holds column (batch row) lr of tile nt, gathered rows r0 + 16*mt + 4*lg + e
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = r0 + 16 * mt + 4 * lg + e;
-      if (i >= nrows) continue;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int b = nt * 16 + lr;
-        if (b >= a.B) continue;
-        if (gridDim.y > 1) a.kpart[((long long)blockIdx.y * a.B + b) * a.kld + i] = acc[mt][nt][e];
-        else rows_store(a, i, b, acc[mt][nt][e]);
-      }
-    }
-}
-
-// Long up-projections: a block of 4 waves owns 64 gathered rows (a 16-row MFMA tile per wave)
-// over the whole of K, staged through LDS in chunks of kRowsKC: one load instruction of a
+// Up-projections: a block of 4 waves owns 64 gathered rows (a 16-row MFMA tile per wave) over
+// its slice of K (all of K unless a short launch splits K over blocks; then each slice writes
+// partial sums that the finishing kernel adds in slice order), staged through LDS in chunks of
+// kRowsKC: one load instruction of a
 // wave covers 2 rows x 512 contiguous bytes, and the activation rows (and their remainders)
 // are staged once per block instead of once per wave. The next chunk's loads are in flight
 // while the MFMAs consume the current one. No cross-wave sum: each wave owns its rows.
@@ -395,8 +256,12 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
   f4v acc[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
-  load(0);
-  for (int k0 = 0; k0 < a.d; k0 += kRowsKC) {   // block-uniform
+  // K chunks of this block's slice (grid.y slices when K is split over blocks)
+  const int nch = (a.d + kRowsKC - 1) / kRowsKC;
+  const int kfirst = (int)((long long)nch * blockIdx.y / gridDim.y) * kRowsKC;
+  const int klast = min(a.d, (int)((long long)nch * (blockIdx.y + 1) / gridDim.y) * kRowsKC);
+  if (kfirst < klast) load(kfirst);
+  for (int k0 = kfirst; k0 < klast; k0 += kRowsKC) {   // block-uniform
     __syncthreads();   // the previous chunk's readers are done
 #pragma unroll
     for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4*>(&s_w[(lrow + 8 * q) * kRowsLdk + kk]) = wreg[q];
@@ -405,7 +270,7 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
 #pragma unroll
       for (int p = 0; p < XLD; ++p) *reinterpret_cast<h8v*>(&s_x[x][(lrow + 8 * p) * kRowsLdk + kk]) = xreg[x][p];
     __syncthreads();
-    if (k0 + kRowsKC < a.d) load(k0 + kRowsKC);
+    if (k0 + kRowsKC < klast) load(k0 + kRowsKC);
     const int nks = min(kRowsKC, a.d - k0 + 31) / 32;   // k-steps holding data (the rest are zero)
     for (int ks = 0; ks < nks; ++ks) {
       const h8v af = *reinterpret_cast<const h8v*>(&s_w[(16 * wv + lr) * kRowsLdk + 32 * ks + 8 * lg]);
@@ -428,7 +293,9 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const int b = nt * 16 + lr;
-      if (b < a.B) rows_store(a, i, b, acc[nt][e]);
+      if (b >= a.B) continue;
+      if (gridDim.y > 1) a.kpart[((long long)blockIdx.y * a.B + b) * a.kld + i] = acc[nt][e];
+      else rows_store(a, i, b, acc[nt][e]);
     }
   }
 }
@@ -618,79 +485,33 @@ hipError_t launch_rows_norm_f16(const float* x, long long ldx, const float* g, i
 }
 
 template <int NT, bool SPLIT>
-static void launch_rows_cfg(const GemmRowsArgs& a, int max_rows, int cus, hipStream_t s) {
-  // more row tiles per wave share the activation fragments; short launches split K over
-  // 8-16 waves per block instead of 4 so that enough waves stream weights
-  constexpr int MTB = NT == 2 ? 4 : 2;
-  const int tiles = (max_rows + 15) / 16;
-  const bool big = (tiles + MTB - 1) / MTB >= cus;
-  if (big && (NT == 2 || a.B > 4)) {
-    hipLaunchKernelGGL((gemm_rows_kernel<NT, SPLIT, MTB, 4>), dim3((tiles + MTB - 1) / MTB), dim3(4 * kWave), 0, s, a);
-  } else if (tiles >= 2 * cus) {
-    hipLaunchKernelGGL((gemm_rows_kernel<NT, SPLIT, 1, 4>), dim3(tiles), dim3(4 * kWave), 0, s, a);
-  } else {   // 16 waves (8 when two batch tiles need the registers)
-    constexpr int KW = NT == 2 ? 8 : 16;
-    hipLaunchKernelGGL((gemm_rows_kernel<NT, SPLIT, 1, KW>), dim3(tiles), dim3(KW * kWave), 0, s, a);
-  }
+static void launch_rows_lds(const GemmRowsArgs& a, int max_rows, int ks, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_rows_lds_kernel<NT, SPLIT>), dim3((max_rows + 63) / 64, ks), dim3(256), 0, s, a);
 }
 
-#ifndef DV_ROWS_LDS
-#define DV_ROWS_LDS 1
-#endif
-
-// A short launch (fewer row tiles than CUs) splits K over blocks: slice q of every tile
-// writes its partial sums, and the finishing kernel adds the slices in order.
-template <int NT, bool SPLIT>
-static void launch_rows_ksplit(const GemmRowsArgs& a, int max_rows, int ks, hipStream_t s) {
-  const int tiles = (max_rows + 15) / 16;
-  hipLaunchKernelGGL((gemm_rows_kernel<NT, SPLIT, 1, 4>), dim3(tiles, ks), dim3(4 * kWave), 0, s, a);
-}
-
+// A short launch (fewer 64-row tiles than twice the CUs) splits K over blocks, up to
+// kRowsMaxSplit slices of whole chunks, and the finishing kernel adds the slices in order.
 hipError_t launch_gemm_rows(const GemmRowsArgs& a_in, int max_rows, int cus, hipStream_t s) {
   GemmRowsArgs a = a_in;
   if (a.d % 8 != 0 || a.B < 1 || a.B > kBatchMax || max_rows < 0) return hipErrorInvalidValue;   // tail K steps are guarded
   if (max_rows == 0) return hipSuccess;
   const bool split = a.X_lo != nullptr;
-  const int tiles = (max_rows + 15) / 16;
-  const int nk = (a.d + 31) / 32;
+  const int tiles = (max_rows + 63) / 64;
+  const int nch = (a.d + kRowsKC - 1) / kRowsKC;
   int ks = 1;
-  if (a.kpart != nullptr && max_rows <= kRowsSplitMaxRows && tiles < cus && a.kld >= max_rows)
-    ks = std::max(1, std::min({(2 * cus + tiles - 1) / tiles, nk / 8, kRowsMaxSplit}));
-  if (ks > 1) {
-    a.ksplit = ks;
-    if (a.B <= 16) {
-      if (split) launch_rows_ksplit<1, true>(a, max_rows, ks, s);
-      else launch_rows_ksplit<1, false>(a, max_rows, ks, s);
-    } else {
-      if (split) launch_rows_ksplit<2, true>(a, max_rows, ks, s);
-      else launch_rows_ksplit<2, false>(a, max_rows, ks, s);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_rows_finish_kernel, dim3((max_rows + 255) / 256, a.B), dim3(256), 0, s, a);
-    return hipGetLastError();
-  }
-  a.ksplit = 1;
-#if DV_ROWS_LDS
-  if (max_rows > kRowsSplitMaxRows || ks == 1) {
-    const dim3 grid((max_rows + 63) / 64);
-    if (a.B <= 16) {
-      if (split) hipLaunchKernelGGL((gemm_rows_lds_kernel<1, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gemm_rows_lds_kernel<1, false>), grid, dim3(256), 0, s, a);
-    } else {
-      if (split) hipLaunchKernelGGL((gemm_rows_lds_kernel<2, true>), grid, dim3(256), 0, s, a);
-      else hipLaunchKernelGGL((gemm_rows_lds_kernel<2, false>), grid, dim3(256), 0, s, a);
-    }
-    return hipGetLastError();
-  }
-#endif
+  if (a.kpart != nullptr && max_rows <= kRowsSplitMaxRows && tiles < 2 * cus && a.kld >= max_rows)
+    ks = std::max(1, std::min({(2 * cus + tiles - 1) / tiles, nch, kRowsMaxSplit}));
+  a.ksplit = ks;
   if (a.B <= 16) {
-    if (split) launch_rows_cfg<1, true>(a, max_rows, cus, s);
-    else launch_rows_cfg<1, false>(a, max_rows, cus, s);
+    if (split) launch_rows_lds<1, true>(a, max_rows, ks, s);
+    else launch_rows_lds<1, false>(a, max_rows, ks, s);
   } else {
-    if (split) launch_rows_cfg<2, true>(a, max_rows, cus, s);
-    else launch_rows_cfg<2, false>(a, max_rows, cus, s);
+    if (split) launch_rows_lds<2, true>(a, max_rows, ks, s);
+    else launch_rows_lds<2, false>(a, max_rows, ks, s);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ks == 1) return e;
+  hipLaunchKernelGGL(gemm_rows_finish_kernel, dim3((max_rows + 255) / 256, a.B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
