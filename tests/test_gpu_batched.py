@@ -1,4 +1,4 @@
-"""Batched decode against the fp64 oracle applied row by row (GPU). Batches of 8..32 rows
+"""Batched decode against the fp64 oracle applied row by row (GPU). Batches of 4..32 rows
 with fp16 weights run on the union of the rows' selections (matrix cores); smaller batches
 run row by row; both are covered.
 

@@ -156,7 +156,7 @@ def test_ragged_rows_match_oracle_per_row(dv, lengths):
             ref = oracle.layer(h[l][b:b + 1], host[l], kcs[l][b:b + 1], vcs[l][b:b + 1], T, io[l][b:b + 1],
                                ho[l][b:b + 1])
             assert_close(h[l + 1][b:b + 1], ref["out"], w.dtype, f"row {b} (T={T}) layer {l}",
-                         batch=B if B >= 8 else 1)
+                         batch=B if B >= 4 else 1)
             for hd in range(w.n_heads):
                 changed = np.flatnonzero(np.any(kc2[l][b, hd] != kcs[l][b, hd], axis=-1) |
                                          np.any(vc2[l][b, hd] != vcs[l][b, hd], axis=-1))
