@@ -74,6 +74,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serial", action="store_true", help="run the predictor on the main stream")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    ap.add_argument("--batch-sizes", default="1,2,4,8,16,32",
+                    help="batch sizes of --workload batched (comma-separated, each 1..32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--workload", choices=["stack", "batched", "sweep", "blocked", "decode", "train"], default="stack",
@@ -380,7 +382,10 @@ def run_batched(args, log):
     vc = sdev.kv_on_device(wb, "v_cache", 0)
     steps = max(5, min(args.steps, 30))
     points = []
-    for B in (1, 2, 4, 8, 16, 32):
+    sizes = [int(v) for v in args.batch_sizes.split(",") if v.strip()]
+    if not sizes or any(not 1 <= B <= Bmax for B in sizes):
+        raise SystemExit(f"--batch-sizes must list values in 1..{Bmax}")
+    for B in sizes:
         wB = w.with_(batch=B)
         zs_m = torch.from_numpy(synth.zipf_scores(wB, w.d_ffn, "sel_mlp")).cuda()
         zs_h = torch.from_numpy(synth.zipf_scores(wB, w.n_heads, "sel_head")).cuda()
