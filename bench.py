@@ -87,8 +87,8 @@ def main() -> int:
                          "predictor training and recall on the OPT-125m-shaped layer")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
-              "multi-GPU path; see DESIGN.md for how the step would shard).", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library has no "
+              "multi-GPU path).", file=sys.stderr)
         return 2
 
     import numpy as np

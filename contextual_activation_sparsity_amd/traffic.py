@@ -12,7 +12,7 @@ Two models live here:
   neuron fraction, and a memory-bound decode step takes at least traffic /
   bandwidth. The page's worked example (LLaMA-3-70B shapes, SwiGLU, so three
   MLP matrices) pins these functions in the tests.
-* This build's algorithmic bytes per layer-token: every weight row, bias, gain
+* The algorithmic bytes counted here per layer-token: every weight row, bias, gain
   and KV entry the sparse step must read, the KV entries it appends and the
   residual-stream vector it reads and writes. Intermediates a fused kernel
   could keep on chip (scores, q/k/v, partial sums) are not counted.

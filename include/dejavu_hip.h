@@ -12,7 +12,7 @@
  *     output-projection weights and none of its KV cache.
  *   - "Pipelined Overlap Execution": the prediction for layer l+1 runs on its own stream
  *     while layer l computes.
- * The survey page "Deja Vu: How Contextual Sparsity Accelerates LLM Inference by 6x"
+ * The summary page "Deja Vu: How Contextual Sparsity Accelerates LLM Inference by 6x"
  * ("What Is Contextual Sparsity?") gives the sparsity levels the workloads use.
  *
  * Conventions for every call

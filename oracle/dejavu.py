@@ -252,7 +252,7 @@ def stack_layer(h_in, t: Dict[str, np.ndarray], t_next: Optional[Dict[str, np.nd
     Execution": the sets of layer l+1 are predicted from an activation that
     exists before layer l+1 starts, so the prediction overlaps layer l. Here
     the predictor of layer l+1 reads the input of layer l, h_l (the reading
-    recorded for this build), and layer l runs with the sets S_l given.
+    taken here), and layer l runs with the sets S_l given.
 
     Returns the layer outputs plus the next layer's scores and sets.
     """

@@ -16,7 +16,7 @@ import torch
 import oracle
 import synth
 
-NORTH_STAR_TOL = 2e-2
+LAYER_TOL = 2e-2
 FP16_BAR = 1e-3
 FP32_BAR = 1e-4
 SCORE_TOL = 1e-3
@@ -68,7 +68,7 @@ def assert_close(got, ref, dtype: str, what: str, batch: int = 1):
     bar = FP16_BAR if dtype == "f16" else FP32_BAR
     if dtype == "f16" and batch >= 2:
         bar = BATCHED_BAR
-    assert err <= NORTH_STAR_TOL * scale, f"{what}: max-abs {err:.3e} > {NORTH_STAR_TOL} * RMS {scale:.3e}"
+    assert err <= LAYER_TOL * scale, f"{what}: max-abs {err:.3e} > {LAYER_TOL} * RMS {scale:.3e}"
     assert err <= bar * scale, f"{what}: max-abs {err:.3e} > internal bar {bar} * RMS {scale:.3e}"
     return err / scale
 

@@ -8,7 +8,7 @@ log-popularity, the batched workload's selection rule), so the rows overlap the 
 batched workload's do. The batched path rounds the activations (normalised inputs, ReLU
 outputs, attention outputs, predictor stage-1 outputs) to fp16 for the matrix cores; its
 internal bar BATCHED_BAR allows for that rounding (about 2^-11 relative per operand),
-and the spec bar 2e-2 * RMS(ref) applies unchanged. The predictor's activations are
+and the layer bar 2e-2 * RMS(ref) applies unchanged. The predictor's activations are
 split into fp16 high parts and remainders, so its scores meet the single-row bar.
 """
 import numpy as np
@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import synth
-from helpers import (BATCHED_BAR, NORTH_STAR_TOL, W_C2, W_RAG16, assert_scores_close, dims_of, kv_host, layer_weights,
+from helpers import (BATCHED_BAR, LAYER_TOL, W_C2, W_RAG16, assert_scores_close, dims_of, kv_host, layer_weights,
                      pred_weights, random_sets, rms, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +35,7 @@ def close(got, ref, what, bar=BATCHED_BAR):
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     scale = max(rms(ref), 1e-30)
     err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
-    assert err <= NORTH_STAR_TOL * scale, f"{what}: max-abs {err:.3e} > {NORTH_STAR_TOL} * RMS {scale:.3e}"
+    assert err <= LAYER_TOL * scale, f"{what}: max-abs {err:.3e} > {LAYER_TOL} * RMS {scale:.3e}"
     assert err <= bar * scale, f"{what}: max-abs {err:.3e} > batched bar {bar} * RMS {scale:.3e}"
     return err / scale
 

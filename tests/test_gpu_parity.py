@@ -183,7 +183,7 @@ def test_sparse_attn(dv, host_layers, w, case):
                     floor = BATCHED_BAR if (w.dtype == "f16" and B >= 2) else 1e-4
                     err = np.abs(got_c[b, h, T].astype(np.float64) - r)
                     assert np.all(err <= ulp * np.abs(r) + floor * rms(r)), f"appended {name}"
-                    assert np.max(err) <= 2e-2 * rms(r), f"appended {name}: north-star bar"
+                    assert np.max(err) <= 2e-2 * rms(r), f"appended {name}: layer bar"
 
                     kg_ = got_c[b, h].copy()
                     kg_[T] = (kc if name == "k" else vc)[b, h, T]
