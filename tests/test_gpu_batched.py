@@ -208,3 +208,49 @@ def test_batched_stack_two_streams_equal_serial(dv):
     for l in range(n):
         ref = oracle.layer(h2[l], host[l], kcs[l], vcs[l], w.t_past, io2[l], ho2[l])
         close(h2[l + 1], ref["out"], f"layer {l} output")
+
+
+@pytest.mark.timeout(900)
+def test_opt175b_batched_full_size_sampled_rows(dv):
+    """The OPT-175B-shaped layer at B = 32 (KV 1024, Zipf selections) on the union path, in
+    the launch configuration the batched bench times; three sampled rows checked against the
+    oracle on their regenerated selected rows (output, MLP part and the appended k/v), and
+    the batched predictor's scores of those rows against the oracle's."""
+    import synth.device as sdev
+    from helpers import oracle_layer_compact, predictor_host
+    w = synth.OPT175B_BATCHED.with_(batch=32)
+    B = w.batch
+    dims = dims_of(w)
+    t = sdev.layer_on_device(w, 0)
+    kc = sdev.kv_on_device(w, "k_cache", 0)
+    vc = sdev.kv_on_device(w, "v_cache", 0)
+    S = zipf_sets(w, B, w.d_ffn, w.k, "sel_mlp")
+    Sh = zipf_sets(w, B, w.n_heads, w.kh, "sel_head")
+    x = synth.x_input(w, step=5)
+    xd = torch.from_numpy(x).cuda()
+    out = torch.empty_like(xd)
+    s_m = torch.empty(B, w.d_ffn, device="cuda")
+    s_h = torch.empty(B, w.n_heads, device="cuda")
+    ws = dv.workspace(dims, B, w.k, w.kh)
+    dv.dv_predict(dims, pred_weights(t), xd, s_m, s_h, ws)
+    dv.dv_layer_step(dims, layer_weights(t), None, xd, None, w.k, w.kh, torch.from_numpy(S).cuda(),
+                     torch.from_numpy(Sh).cuda(), kc, vc, w.t_past, out, ws=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    gm, gh = s_m.cpu().numpy(), s_h.cpu().numpy()
+    rows = (0, 13, 31)
+    p = predictor_host(w, 0)
+    rm, rh = oracle.predict(p["p1_mlp"], p["p2_mlp"], p["p1_head"], p["p2_head"], x[list(rows)])
+    assert_scores_close(gm[list(rows)], rm, "full-size s_mlp")
+    assert_scores_close(gh[list(rows)], rh, "full-size s_head")
+    for b in rows:
+        ref = oracle_layer_compact(w, 0, x[b], S[b], Sh[b], b)
+        close(got[b:b + 1], ref["out"], f"row {b} layer out")
+        close(got[b:b + 1] - ref["h1"], ref["y_m"], f"row {b} y_m")
+        for j, h in enumerate(Sh[b]):
+            for m, cache in ((1, kc), (2, vc)):
+                slot = cache[b, h, w.t_past].float().cpu().numpy().astype(np.float64)
+                r = ref["qkv"][0, j, m]
+                assert np.max(np.abs(slot - r)) <= BATCHED_BAR * 4 * max(rms(r), 1e-30) + 2 ** -10 * np.max(np.abs(r))
+    del t, kc, vc, ws
+    torch.cuda.empty_cache()
