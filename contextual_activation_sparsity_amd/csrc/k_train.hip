@@ -6,9 +6,8 @@
 //
 // Loss: mean binary cross-entropy of the scores (logits) over every (sample, output) pair;
 // optimiser: full-batch gradient descent with heavy-ball momentum. The contractions are fp32
-// GEMMs on the vector units (fp32 matrix-core and vector peaks are equal on this chip, and
-// these problems are small and off the decode path); every reduction runs in a fixed order, so
-// a step is bitwise reproducible.
+// GEMMs on the matrix cores; every reduction runs in a fixed order, so a step is bitwise
+// reproducible.
 #include <algorithm>
 
 #include "dv_device.h"
@@ -16,7 +15,6 @@
 
 namespace dv {
 
-constexpr int kGemmTile = 64;
 constexpr int kGemmK = 16;
 constexpr int kGemmThreads = 256;
 constexpr int kLossBlocks = 512;
@@ -64,61 +62,88 @@ hipError_t launch_fire(const float* a, long long n, uint8_t* fire, hipStream_t s
 }
 
 // ---------------------------------------------------------------------------
-// fp32 GEMM with strided operands: C[i][j] = sum_k A(i,k) B(k,j), A(i,k) = A[i*sai + k*sak],
-// B(k,j) = B[k*sbk + j*sbj]. A 64 x 64 tile per block, K in steps of 16 staged in LDS, 4 x 4
-// outputs per thread. With ksplit > 1, slice z of the K range writes its partial tile to
-// C + z*M*N and a second kernel sums the slices in order.
+// fp32 GEMM with strided operands on the matrix cores: C[i][j] = sum_k A(i,k) B(k,j),
+// A(i,k) = A[i*sai + k*sak], B(k,j) = B[k*sbk + j*sbj]. A 128 x 128 output tile per block of
+// 4 waves (64 x 64 per wave, 4 x 4 tiles of v_mfma_f32_16x16x4f32), K in steps of 16 staged
+// in LDS k-major (each operand loaded along its contiguous axis), the next step's loads in
+// flight during the MFMAs. With more than one slice, slice z of the K range writes its
+// partial tile to C + z*M*N and a second kernel sums the slices in order.
 // ---------------------------------------------------------------------------
+typedef float f4t __attribute__((ext_vector_type(4)));
+constexpr int kMT = 128;                       // output tile edge
+constexpr int kMLd = kMT + 4;                  // padded LDS row (floats)
+constexpr int kMLoads = kMT * kGemmK / kGemmThreads;   // operand elements per thread per step
+
 __global__ __launch_bounds__(kGemmThreads) void gemm_f32_kernel(GemmF32Args a, int k_per_slice) {
-  __shared__ float As[kGemmK][kGemmTile + 4];
-  __shared__ float Bs[kGemmK][kGemmTile + 4];
-  const int tid = threadIdx.x;
-  const int tx = tid % 16, ty = tid / 16;
-  const int i0 = blockIdx.y * kGemmTile, j0 = blockIdx.x * kGemmTile;
+  __shared__ float As[kGemmK][kMLd];
+  __shared__ float Bs[kGemmK][kMLd];
+  const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+  const int lr = lane % 16, lg = lane / 16;
+  const int wi = (wv / 2) * 64, wj = (wv % 2) * 64;   // this wave's 64 x 64 quarter
+  const int i0 = blockIdx.y * kMT, j0 = blockIdx.x * kMT;
   const int kb = blockIdx.z * k_per_slice;
   const int ke = min(a.K, kb + k_per_slice);
   const bool a_kfast = a.sak == 1;
   const bool b_jfast = a.sbj == 1;
-  float acc[4][4] = {};
-  for (int k0 = kb; k0 < ke; k0 += kGemmK) {
+  float ra[kMLoads], rb[kMLoads];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kMLoads; ++q) {
       const int e = tid + q * kGemmThreads;
-      const int ii = a_kfast ? e / kGemmK : e % kGemmTile;
-      const int kk = a_kfast ? e % kGemmK : e / kGemmTile;
+      const int ii = a_kfast ? e / kGemmK : e % kMT;
+      const int kk = a_kfast ? e % kGemmK : e / kMT;
       const int gi = i0 + ii, gk = k0 + kk;
-      As[kk][ii] = (gi < a.M && gk < ke) ? a.A[(long long)gi * a.sai + (long long)gk * a.sak] : 0.f;
-      const int jj = b_jfast ? e % kGemmTile : e / kGemmK;
-      const int k2 = b_jfast ? e / kGemmTile : e % kGemmK;
+      ra[q] = (gi < a.M && gk < ke) ? a.A[(long long)gi * a.sai + (long long)gk * a.sak] : 0.f;
+      const int jj = b_jfast ? e % kMT : e / kGemmK;
+      const int k2 = b_jfast ? e / kMT : e % kGemmK;
       const int gj = j0 + jj, gk2 = k0 + k2;
-      Bs[k2][jj] = (gj < a.N && gk2 < ke) ? a.B[(long long)gk2 * a.sbk + (long long)gj * a.sbj] : 0.f;
+      rb[q] = (gj < a.N && gk2 < ke) ? a.B[(long long)gk2 * a.sbk + (long long)gj * a.sbj] : 0.f;
+    }
+  };
+  f4t acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = f4t{0.f, 0.f, 0.f, 0.f};
+  if (kb < ke) load(kb);
+  for (int k0 = kb; k0 < ke; k0 += kGemmK) {   // block-uniform
+    __syncthreads();   // the previous step's readers are done
+#pragma unroll
+    for (int q = 0; q < kMLoads; ++q) {
+      const int e = tid + q * kGemmThreads;
+      As[a_kfast ? e % kGemmK : e / kMT][a_kfast ? e / kGemmK : e % kMT] = ra[q];
+      Bs[b_jfast ? e / kMT : e % kGemmK][b_jfast ? e % kMT : e / kGemmK] = rb[q];
     }
     __syncthreads();
+    if (k0 + kGemmK < ke) load(k0 + kGemmK);
 #pragma unroll
-    for (int kk = 0; kk < kGemmK; ++kk) {
+    for (int ks = 0; ks < kGemmK / 4; ++ks) {
+      const int k = 4 * ks + lg;   // A: row lr, k = lg; B: column lr, k = lg
       float av[4], bv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = As[kk][ty * 4 + r];
+      for (int m = 0; m < 4; ++m) av[m] = As[k][wi + 16 * m + lr];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = Bs[kk][tx * 4 + c];
+      for (int n = 0; n < 4; ++n) bv[n] = Bs[k][wj + 16 * n + lr];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] = fmaf(av[r], bv[c], acc[r][c]);
+        for (int n = 0; n < 4; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[m], bv[n], acc[m][n], 0, 0, 0);
     }
-    __syncthreads();
   }
+  // D layout: lane holds column lr of its tile, rows 4*lg + e
   float* C = a.C + (long long)blockIdx.z * a.M * a.N;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int gi = i0 + ty * 4 + r;
-    if (gi >= a.M) continue;
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int gj = j0 + tx * 4 + c;
-      if (gj < a.N) C[(long long)gi * a.N + gj] = acc[r][c];
+    for (int e = 0; e < 4; ++e) {
+      const int gi = i0 + wi + 16 * m + 4 * lg + e;
+      if (gi >= a.M) continue;
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int gj = j0 + wj + 16 * n + lr;
+        if (gj < a.N) C[(long long)gi * a.N + gj] = acc[m][n][e];
+      }
     }
-  }
 }
 
 __global__ void sum_slices_kernel(const float* part, int slices, long long n, float* out) {
@@ -130,7 +155,7 @@ __global__ void sum_slices_kernel(const float* part, int slices, long long n, fl
 }
 
 int gemm_f32_slices(int M, int N, int K, int cus) {
-  const long long tiles = (long long)((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile);
+  const long long tiles = (long long)((M + kMT - 1) / kMT) * ((N + kMT - 1) / kMT);
   const long long want = 2LL * cus;
   int ks = (int)std::min<long long>((want + tiles - 1) / tiles, std::max(1, K / 256));
   return std::max(1, std::min(ks, kGemmMaxSlices));
@@ -145,7 +170,7 @@ hipError_t launch_gemm_f32(GemmF32Args a, int slices, float* scratch, hipStream_
   slices = std::max(1, (a.K + kps - 1) / kps);
   float* dst = a.C;
   if (slices > 1) a.C = scratch;
-  dim3 grid((a.N + kGemmTile - 1) / kGemmTile, (a.M + kGemmTile - 1) / kGemmTile, slices);
+  dim3 grid((a.N + kMT - 1) / kMT, (a.M + kMT - 1) / kMT, slices);
   hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(kGemmThreads), 0, s, a, std::max(kps, 1));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || slices == 1) return e;
