@@ -9,8 +9,8 @@ import torch
 
 import oracle
 import synth
-from helpers import (BATCHED_BAR, W_C1, W_C2, W_RAG16, W_RAG32, assert_close, assert_scores_close, dims_of, kv_host,
-                     layer_weights, pred_weights, random_sets, rms, to_dev)
+from helpers import (BATCHED_BAR, W_C1, W_C2, W_RAG16, W_RAG32, assert_close, assert_scores_close, chosen_sets, dims_of,
+                     kv_host, layer_weights, pred_weights, random_sets, rms, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -238,20 +238,25 @@ def test_layer_step_inline_prediction(dv, host_layers, w):
     t = host_layers[w.name]
     x = synth.x_input(w, step=9)
     got, io, ho, _ = run_layer(dv, w, t, x, inline=True)
-    # the sets used are exactly the top-k of the GPU's own scores
+    # inside the library: the sets used are the top-k of its own scores (GPU against GPU)
     dims = dims_of(w)
     d = to_dev({k_: t[k_] for k_ in ("p1_mlp", "p2_mlp", "p1_head", "p2_head")})
     s_m = torch.empty(1, w.d_ffn, device="cuda")
     s_h = torch.empty(1, w.n_heads, device="cuda")
     dv.dv_predict(dims, pred_weights(d), torch.from_numpy(x).cuda(), s_m, s_h, dv.workspace(dims, 1, w.k, w.kh))
+    tm = torch.empty(1, w.k, dtype=torch.int32, device="cuda")
+    th = torch.empty(1, w.kh, dtype=torch.int32, device="cuda")
+    dv.dv_topk(s_m, w.k, tm)
+    dv.dv_topk(s_h, w.kh, th)
     torch.cuda.synchronize()
-    gs_m, gs_h = s_m.cpu().numpy(), s_h.cpu().numpy()
-    assert np.array_equal(io, oracle.topk(gs_m, w.k))
-    assert np.array_equal(ho, oracle.topk(gs_h, w.kh))
+    assert np.array_equal(io, tm.cpu().numpy()) and np.array_equal(ho, th.cpu().numpy())
+    # against the oracle's own prediction, selection and layer on the same seeded input
     rm, rh = oracle.predict(t["p1_mlp"], t["p2_mlp"], t["p1_head"], t["p2_head"], x)
-    assert_scores_close(gs_m, rm, "s_mlp")
-    assert_scores_close(gs_h, rh, "s_head")
-    ref = oracle.layer(x, t, kv_host(w, "k_cache"), kv_host(w, "v_cache"), w.t_past, io, ho)
+    assert_scores_close(s_m.cpu().numpy(), rm, "s_mlp")
+    assert_scores_close(s_h.cpu().numpy(), rh, "s_head")
+    S = chosen_sets(io, rm, w.k, "neuron set")
+    Sh = chosen_sets(ho, rh, w.kh, "head set")
+    ref = oracle.layer(x, t, kv_host(w, "k_cache"), kv_host(w, "v_cache"), w.t_past, S, Sh)
     assert_close(got, ref["out"], w.dtype, "layer out (inline sets)")
 
 
