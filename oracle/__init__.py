@@ -26,7 +26,7 @@ on tiny inputs and the printed worked example; each function's docstring
 names its pins.
 """
 from .dejavu import (  # noqa: F401
-    predict, topk, topk_order_key, rmsnorm, qkv_all_heads, attention, mlp, layer, stack_layer,
+    predict, topk, topk_order_key, rmsnorm, qkv_all_heads, attention, mlp, layer,
     masks_from_sets, block_scores, expand_blocks, RMS_EPS,
 )
 from .train import (  # noqa: F401

@@ -241,26 +241,3 @@ def layer(x, t: Dict[str, np.ndarray], k_cache, v_cache, t_past: int,
     ff = mlp(xn2, t["w1t"], t["b1"], t["w2"], t["b2"], masks_from_sets(neuron_sets, F))
     return {"out": h1 + ff["y_m"], "h1": h1, "y_a": att["y_a"], "y_m": ff["y_m"],
             "xn1": xn1, "xn2": xn2, "qkv": att["qkv"], "o": att["o"], "u": ff["u"]}
-
-
-def stack_layer(h_in, t: Dict[str, np.ndarray], t_next: Optional[Dict[str, np.ndarray]],
-                k_cache, v_cache, t_past: int, neuron_sets, head_sets,
-                k: int, kh: int) -> Dict[str, np.ndarray]:
-    """One layer of the lookahead stack, checked with teacher forcing.
-
-    DejaVu Guide, "Asynchronous Lookahead Predictors" and "Pipelined Overlap
-    Execution": the sets of layer l+1 are predicted from an activation that
-    exists before layer l+1 starts, so the prediction overlaps layer l. Here
-    the predictor of layer l+1 reads the input of layer l, h_l (the reading
-    taken here), and layer l runs with the sets S_l given.
-
-    Returns the layer outputs plus the next layer's scores and sets.
-    """
-    out = layer(h_in, t, k_cache, v_cache, t_past, neuron_sets, head_sets)
-    if t_next is not None:
-        s_m, s_h = predict(t_next["p1_mlp"], t_next["p2_mlp"], t_next["p1_head"],
-                           t_next["p2_head"], h_in)
-        out["next_s_mlp"], out["next_s_head"] = s_m, s_h
-        out["next_sets"] = topk(s_m.astype(np.float32), k)
-        out["next_heads"] = topk(s_h.astype(np.float32), kh)
-    return out
