@@ -22,7 +22,7 @@ In the pages' row-vector notation: a = x . W1 is ``w1t @ x``, and u . W2 is
 from __future__ import annotations
 
 import math
-from typing import Dict, Optional, Sequence, Tuple
+from typing import Dict, Sequence, Tuple
 
 import numpy as np
 
