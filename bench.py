@@ -164,6 +164,7 @@ def main() -> int:
     # (2) the whole two-stream step captured once in a HIP graph and replayed (fresh x is
     #     copied into the graph's input buffer before each replay)
     ms_graph = None
+    step_dist = None
     if not args.no_graph:
         x_in = torch.empty(1, w.d_model, device="cuda")
         x_in.copy_(xs[0])
@@ -180,6 +181,19 @@ def main() -> int:
             gstep(i)
         ms_graph, wall_graph = timed(gstep, args.steps)
         log(f"[bench] graph: {ms_graph:.3f} ms/step ({ms_graph * 1e3 / L:.2f} us/layer-token, host {wall_graph:.3f} ms)")
+        # distribution: replays timed one by one (synchronised in between; not the headline)
+        per = []
+        for i in range(min(50, args.steps)):
+            x_in.copy_(xs[args.warmup + i])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / L)
+        step_dist = {"p10": round(float(np.percentile(per, 10)), 3), "p50": round(float(np.median(per)), 3),
+                     "p90": round(float(np.percentile(per, 90)), 3), "replays": len(per)}
+        log(f"[bench] per-replay us/layer-token: {step_dist}")
 
     # (3) eager again with HIP event pairs around every q/k/v gather launch (on its stream)
     n_ev = args.steps * L
@@ -191,6 +205,11 @@ def main() -> int:
     assert got == n_ev, f"timing hook recorded {got} of {n_ev}"
     qkv_ms = np.array(qkv_ms[:n_ev], dtype=np.float64)
     log(f"[bench] instrumented eager pass: {ms_hooked:.3f} ms/step")
+
+    # plain streaming read on the same GPU (4 GiB, every byte loaded once), best of 5: the
+    # reference a read-only kernel reaches here, reported beside the 8 TB/s peak
+    stream_read = sdev.stream_read_gbps()
+    log(f"[bench] plain streaming read: {stream_read:.0f} GB/s")
 
     ms_per_step = ms_graph if ms_graph is not None else ms_eager
     us_per_layer = ms_per_step * 1e3 / L
@@ -239,7 +258,10 @@ def main() -> int:
                      "kernel": "rowdot_kernel<f16,256,6,qkv>: head-sparse q/k/v gather-GEMV + next layer's "
                                "predictor stage 1",
                      "bytes_per_launch": int(round(launch_bytes.mean())), "avg_launch_us": round(qkv_avg_us, 3),
-                     "launches_timed": int(n_ev)},
+                     "launches_timed": int(n_ev), "stream_read_GBps": round(stream_read, 1),
+                     "frac_of_stream_read": round(qkv_gbps / stream_read, 4)},
+        "us_per_layer_token_per_replay": step_dist,
+        "step_pct_of_stream_read": round(100.0 * gbps / stream_read, 2),
     }
 
     if not args.no_dense:

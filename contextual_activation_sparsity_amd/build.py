@@ -2,7 +2,8 @@
 
 * contextual_activation_sparsity_amd/libdejavu_hip.so : the sparse layer step (C ABI in
   include/dejavu_hip.h)
-* synth/libdv_synth.so : the device filler of the seeded synthetic inputs
+* synth/libdv_synth.so : the device filler of the seeded synthetic inputs, and the plain
+                         streaming-read kernel the bench reports as its read reference
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instructions disabled.
 """
@@ -19,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdejavu_hip.so")
 SYNTH_SRC = os.path.join(ROOT, "synth", "fill.hip")
+SYNTH_STREAM_SRC = os.path.join(ROOT, "synth", "stream.hip")
 SYNTH_LIB = os.path.join(ROOT, "synth", "libdv_synth.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -49,6 +51,8 @@ def build(verbose: bool = False, jobs: int = 8) -> None:
         cmds.append([HIPCC, *FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o])
     synth_obj = os.path.join(BUILD, "synth_fill.o")
     cmds.append([HIPCC, *FLAGS, "-c", SYNTH_SRC, "-o", synth_obj])
+    stream_obj = os.path.join(BUILD, "synth_stream.o")
+    cmds.append([HIPCC, *FLAGS, "-c", SYNTH_STREAM_SRC, "-o", stream_obj])
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
@@ -57,7 +61,7 @@ def build(verbose: bool = False, jobs: int = 8) -> None:
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
     os.replace(tmp, LIB)
     tmp = SYNTH_LIB + ".tmp"
-    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, synth_obj])
+    _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, synth_obj, stream_obj])
     os.replace(tmp, SYNTH_LIB)
     if verbose:
         print("built", LIB, SYNTH_LIB)

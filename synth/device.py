@@ -1,4 +1,5 @@
-"""Device-side generation of the seeded synthetic inputs (bit-identical to synth's host draws).
+"""Device-side generation of the seeded synthetic inputs (bit-identical to synth's host draws),
+and a plain streaming-read measurement for the bench.
 
 Large workloads (the OPT-175B-shaped 24-layer stack holds ~93 GB of fp16 weights, caches
 and predictors) are drawn directly in HBM by synth/libdv_synth.so; the host regenerates any
@@ -28,6 +29,9 @@ def _lib():
         L.dv_synth_fill.restype = ctypes.c_int
         L.dv_synth_fill.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_ulonglong,
                                     ctypes.c_float, ctypes.c_longlong, ctypes.c_void_p]
+        L.dv_synth_stream_read.restype = ctypes.c_int
+        L.dv_synth_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p]
         _LIB = L
     return _LIB
 
@@ -77,3 +81,26 @@ def x_on_device(w: Workload, step: int = 0, layer: int = 0, device="cuda") -> to
 
 def to_device(arrs: Dict[str, np.ndarray], device="cuda") -> Dict[str, torch.Tensor]:
     return {k: torch.from_numpy(np.ascontiguousarray(v)).to(device) for k, v in arrs.items()}
+
+
+def stream_read_gbps(nbytes: int = 4 << 30, reps: int = 5) -> float:
+    """Best read bandwidth (GB/s) of the plain streaming-read kernel over a device buffer of
+    nbytes (well beyond the 256 MB Infinity Cache), timed with HIP events on the current stream.
+    A measurement reference for the bench; it draws no numbers."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    blocks = 8 * props.multi_processor_count
+    sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    best = 0.0
+    for _ in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = _lib().dv_synth_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream)
+        e1.record()
+        if rc != 0:
+            raise RuntimeError(f"dv_synth_stream_read failed with hip error {rc}")
+        torch.cuda.synchronize()
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf, sink
+    return best
