@@ -947,9 +947,12 @@ dv_status run_stack(const dv_dims* dims, const dv_layer* layers, const dv_predic
                      fuse ? p1 : nullptr, fuse ? 2 : 0));
     if (ahead) {
       if (two) DV_HIP(hipStreamWaitEvent(st_side, di->ev_in, 0));
+      // Stage 2 is planned for three quarters of the CUs: it starts together with layer l's
+      // attention, and a grid over every CU holds them all while attention waits (measured on
+      // the 24-layer OPT-175B-shaped stack: 123.9 against 126.9 us per layer-token).
       if (fuse)
         DV_TRY(run_predict_stage2(dims, &preds[l + 1], B, at<float>(ws_side, L.s_mlp), at<float>(ws_side, L.s_head),
-                                  at<float>(ws_side, L.z), cus, st_side));
+                                  at<float>(ws_side, L.z), two ? std::max(1, cus * 3 / 4) : cus, st_side));
       else
         DV_TRY(run_predict(dims, &preds[l + 1], h_in(l), B, at<float>(ws_side, L.s_mlp), at<float>(ws_side, L.s_head),
                            L, ws_side, cus, st_side));
