@@ -744,7 +744,8 @@ TrainPlan train_plan(int M, int d, int N, int r) {
   const int outs[5][3] = {{M, r, d}, {M, N, r}, {N, r, M}, {M, r, N}, {r, d, M}};
   size_t scratch = 0;
   for (int i = 0; i < 5; ++i) {
-    p.ks[i] = dv::gemm_f32_slices(outs[i][0], outs[i][1], outs[i][2], 256);
+    // the scores product (i = 1) carries the cross-entropy epilogue, which needs whole sums
+    p.ks[i] = i == 1 ? 1 : dv::gemm_f32_slices(outs[i][0], outs[i][1], outs[i][2], 256);
     if (p.ks[i] > 1) scratch = std::max(scratch, (size_t)p.ks[i] * outs[i][0] * outs[i][1]);
   }
   size_t off = 0;
@@ -755,7 +756,7 @@ TrainPlan train_plan(int M, int d, int N, int r) {
   p.g1 = take((size_t)r * d);
   p.g2 = take((size_t)N * r);
   p.scratch = take(scratch);
-  p.part = take((size_t)dv::loss_parts());
+  p.part = take((size_t)dv::gemm_f32_blocks(M, N));
   p.total = off;
   return p;
 }
@@ -790,10 +791,15 @@ dv_status dv_predictor_train_step(const float* x, int32_t M, int32_t d, const ui
   float* scr = at<float>(ws, P.scratch);
   // Z = x P1^T  [M][r]
   DV_HIP(dv::launch_gemm_f32({x, d, 1, p1, 1, d, Z, M, r, d}, P.ks[0], scr, stream));
-  // S = Z P2^T  [M][N]
-  DV_HIP(dv::launch_gemm_f32({Z, r, 1, p2, 1, r, S, M, N, r}, P.ks[1], scr, stream));
-  // G = (sigmoid(S) - y) / (M N) in place, and the loss
-  DV_HIP(dv::launch_bce_grad(S, y, (long long)M * N, at<float>(ws, P.part), loss, stream));
+  // S = Z P2^T  [M][N], turned by the epilogue into G = (sigmoid(S) - y) / (M N), with the
+  // loss terms summed per block; then the loss
+  const float inv_n = 1.f / ((float)M * (float)N);
+  dv::GemmF32Args sg{Z, r, 1, p2, 1, r, S, M, N, r};
+  sg.bce_y = y;
+  sg.bce_part = at<float>(ws, P.part);
+  sg.inv_n = inv_n;
+  DV_HIP(dv::launch_gemm_f32(sg, P.ks[1], scr, stream));
+  DV_HIP(dv::launch_loss_finish(at<float>(ws, P.part), dv::gemm_f32_blocks(M, N), inv_n, loss, stream));
   // dL/dP2 = G^T Z  [N][r]
   DV_HIP(dv::launch_gemm_f32({S, 1, N, Z, r, 1, g2, N, r, M}, P.ks[2], scr, stream));
   // dL/dZ = G P2  [M][r]

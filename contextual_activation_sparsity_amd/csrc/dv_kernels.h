@@ -223,14 +223,21 @@ struct GemmF32Args {
   long long sbk, sbj;
   float* C;
   int M, N, K;
+  // Optional cross-entropy epilogue (one K slice only): with bce_y set, C receives
+  // (sigmoid(S) - y) * inv_n instead of S, and block b adds its loss terms
+  // softplus(s) - y*s in a fixed order into bce_part[b].
+  const uint8_t* bce_y;
+  float* bce_part;
+  float inv_n;
 };
-constexpr int kGemmMaxSlices = 16;
+constexpr int kGemmMaxSlices = 32;
 int gemm_f32_slices(int M, int N, int K, int cus);   // K slices that fill `cus` compute units
 // With slices > 1, scratch holds slices * M * N floats (partial products summed in slice order).
 hipError_t launch_gemm_f32(GemmF32Args a, int slices, float* scratch, hipStream_t s);
-// S [n] scores -> (sigmoid(S) - y) / n in place; *loss = mean cross-entropy (part: loss_parts() floats).
-hipError_t launch_bce_grad(float* S, const uint8_t* y, long long n, float* part, float* loss, hipStream_t s);
-int loss_parts();
+// Blocks of the cross-entropy epilogue of an M x N product (the size of its bce_part array).
+int gemm_f32_blocks(int M, int N);
+// *loss = inv_n * (sum of part[0..n_part) in a fixed order).
+hipError_t launch_loss_finish(const float* part, int n_part, float inv_n, float* loss, hipStream_t s);
 hipError_t launch_momentum_step(float* p1, float* v1, const float* g1, long long n1, float* p2, float* v2,
                                 const float* g2, long long n2, float lr, float mu, hipStream_t s);
 

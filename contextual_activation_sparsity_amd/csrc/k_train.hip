@@ -4,7 +4,8 @@
 // summary "What Is Contextual Sparsity?": the classifiers are trained offline on the dense
 // model's activations, with the layer input as features).
 //
-// Loss: mean binary cross-entropy of the scores (logits) over every (sample, output) pair;
+// Loss: mean binary cross-entropy of the scores (logits) over every (sample, output) pair,
+// computed in the epilogue of the product that forms the scores;
 // optimiser: full-batch gradient descent with heavy-ball momentum. The contractions are fp32
 // GEMMs on the matrix cores; every reduction runs in a fixed order, so a step is bitwise
 // reproducible.
@@ -17,7 +18,6 @@ namespace dv {
 
 constexpr int kGemmK = 16;
 constexpr int kGemmThreads = 256;
-constexpr int kLossBlocks = 512;
 
 // ---------------------------------------------------------------------------
 // Targets
@@ -132,6 +132,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f32_kernel(GemmF32Args a, i
   }
   // D layout: lane holds column lr of its tile, rows 4*lg + e
   float* C = a.C + (long long)blockIdx.z * a.M * a.N;
+  float lsum = 0.f;
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -141,9 +142,30 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_f32_kernel(GemmF32Args a, i
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         const int gj = j0 + wj + 16 * n + lr;
-        if (gj < a.N) C[(long long)gi * a.N + gj] = acc[m][n][e];
+        if (gj >= a.N) continue;
+        const long long o = (long long)gi * a.N + gj;
+        float v = acc[m][n][e];
+        if (a.bce_y) {   // loss term softplus(s) - y s, and the gradient (sigmoid(s) - y) / n
+          const float t = a.bce_y[o] ? 1.f : 0.f;
+          const float ex = expf(-fabsf(v));
+          lsum += fmaxf(v, 0.f) + log1pf(ex) - t * v;
+          const float sig = v >= 0.f ? 1.f / (1.f + ex) : ex / (1.f + ex);
+          v = (sig - t) * a.inv_n;
+        }
+        C[o] = v;
       }
     }
+  if (a.bce_y) {   // block sum in a fixed order: lanes by butterfly, then waves in order
+    __shared__ float s_loss[kGemmThreads / kWave];
+    lsum = group_sum<kWave>(lsum);
+    if (lane == 0) s_loss[wv] = lsum;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.f;
+      for (int w = 0; w < kGemmThreads / kWave; ++w) t += s_loss[w];
+      a.bce_part[blockIdx.y * gridDim.x + blockIdx.x] = t;
+    }
+  }
 }
 
 __global__ void sum_slices_kernel(const float* part, int slices, long long n, float* out) {
@@ -165,6 +187,7 @@ int gemm_f32_slices(int M, int N, int K, int cus) {
 hipError_t launch_gemm_f32(GemmF32Args a, int slices, float* scratch, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.K <= 0 || slices < 1) return hipErrorInvalidValue;
+  if (a.bce_y != nullptr && slices != 1) return hipErrorInvalidValue;   // the epilogue needs whole sums
   int kps = (a.K + slices - 1) / slices;
   kps = (kps + kGemmK - 1) / kGemmK * kGemmK;
   slices = std::max(1, (a.K + kps - 1) / kps);
@@ -180,52 +203,30 @@ hipError_t launch_gemm_f32(GemmF32Args a, int slices, float* scratch, hipStream_
 }
 
 // ---------------------------------------------------------------------------
-// Loss and its gradient with respect to the scores, in place: S becomes
-// G = (sigmoid(S) - y) / n. Block b sums softplus(s) - y*s over its contiguous range into
-// part[b]; the finishing kernel adds the parts in block order.
+// Loss: the cross-entropy epilogue's block parts summed by one block in a fixed order (each
+// thread adds a fixed strided subset in index order, then a pairwise tree over the threads).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bce_grad_kernel(float* S, const uint8_t* y, long long n, float inv_n,
-                                                       long long per_block, float* part) {
-  __shared__ float s_red[256 / kWave];
-  const long long b0 = (long long)blockIdx.x * per_block;
-  const long long b1 = min(n, b0 + per_block);
-  float acc = 0.f;
-  for (long long i = b0 + threadIdx.x; i < b1; i += blockDim.x) {
-    const float s = S[i];
-    const float t = y[i] ? 1.f : 0.f;
-    const float e = expf(-fabsf(s));
-    acc += fmaxf(s, 0.f) + log1pf(e) - t * s;
-    const float sig = s >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
-    S[i] = (sig - t) * inv_n;
-  }
-  acc = group_sum<kWave>(acc);
-  if ((threadIdx.x % kWave) == 0) s_red[threadIdx.x / kWave] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float t = 0.f;
-    for (int w = 0; w < 256 / kWave; ++w) t += s_red[w];
-    part[blockIdx.x] = t;
-  }
-}
-
-__global__ void loss_finish_kernel(const float* part, int n_part, float inv_n, float* loss) {
-  if (threadIdx.x != 0) return;
+constexpr int kFinishThreads = 1024;
+__global__ __launch_bounds__(kFinishThreads) void loss_finish_kernel(const float* part, int n_part, float inv_n,
+                                                                     float* loss) {
+  __shared__ float s_t[kFinishThreads];
   float t = 0.f;
-  for (int i = 0; i < n_part; ++i) t += part[i];
-  *loss = t * inv_n;
+  for (int i = threadIdx.x; i < n_part; i += kFinishThreads) t += part[i];
+  s_t[threadIdx.x] = t;
+  __syncthreads();
+  for (int w = kFinishThreads / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) s_t[threadIdx.x] += s_t[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = s_t[0] * inv_n;
 }
 
-hipError_t launch_bce_grad(float* S, const uint8_t* y, long long n, float* part, float* loss, hipStream_t s) {
-  const float inv_n = 1.f / (float)n;
-  const long long per_block = (n + kLossBlocks - 1) / kLossBlocks;
-  hipLaunchKernelGGL(bce_grad_kernel, dim3(kLossBlocks), dim3(256), 0, s, S, y, n, inv_n, per_block, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(loss_finish_kernel, dim3(1), dim3(64), 0, s, part, kLossBlocks, inv_n, loss);
+hipError_t launch_loss_finish(const float* part, int n_part, float inv_n, float* loss, hipStream_t s) {
+  hipLaunchKernelGGL(loss_finish_kernel, dim3(1), dim3(kFinishThreads), 0, s, part, n_part, inv_n, loss);
   return hipGetLastError();
 }
 
-int loss_parts() { return kLossBlocks; }
+int gemm_f32_blocks(int M, int N) { return ((M + kMT - 1) / kMT) * ((N + kMT - 1) / kMT); }
 
 // v = mu v + g; p = p - lr v, over two parameter arrays in one launch.
 __global__ void momentum_step_kernel(float* p1, float* v1, const float* g1, long long n1, float* p2, float* v2,
