@@ -5,8 +5,9 @@
 // row); the union only shares the weight traffic: every selected weight row is read once
 // and multiplied against all B activation rows on the matrix cores.
 //
-//  * union_zero / union_scatter / union_list: per-row bitmaps of the selected groups (neurons
-//    or heads), their OR, and the OR as an ascending list with its length in device memory.
+//  * union_rows / union_or / union_list: per-row bitmaps of the selected groups (neurons or
+//    heads, from the rows' ascending lists by binary search, no atomics), their OR, and the OR
+//    as an ascending list with its length in device memory.
 //  * rows_norm_f16: RMSNorm of each row, rounded to fp16 (the MFMA operand type).
 //  * gemm_rows (up-projection, q/k/v and W1; both predictor factors): out[b][i] =
 //    act(W[row_i] . X[b] + bias), masked per row. A block stages 64 gathered weight rows and
@@ -43,24 +44,38 @@ __device__ __forceinline__ int rank_below(const unsigned* bits, int j) {
 // ---------------------------------------------------------------------------
 // union of the rows' selections
 // ---------------------------------------------------------------------------
-__global__ void union_zero_kernel(UnionArgs a) {
+// Row bitmaps without atomics: thread (row b, word w) finds the first entry >= 32w of the row's
+// ascending list by binary search and sets the bits of the entries below 32(w+1) (entries
+// outside [0, n) select nothing). Every word is written whole, so no clearing pass is needed.
+__global__ void union_rows_kernel(UnionArgs a) {
   const UnionProb& P = blockIdx.y == 0 ? a.p[0] : a.p[1];
   const int words = (P.n + 31) / 32;
-  const int total = (a.B + 1) * words;   // B row bitmaps + the union
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) P.bits[i] = 0u;
+  const long long total = (long long)a.B * words;
+  for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
+       t += (long long)gridDim.x * blockDim.x) {
+    const int b = (int)(t / words), w = (int)(t - (long long)b * words);
+    const int32_t* L = P.idx + (long long)b * P.idx_bstride;
+    const int lo_v = 32 * w, hi_v = min(32 * w + 32, P.n);
+    int lo = 0, hi = P.k;   // first position with L[pos] >= lo_v
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (L[mid] < lo_v) lo = mid + 1;
+      else hi = mid;
+    }
+    unsigned m = 0u;
+    for (int i = lo; i < P.k && L[i] < hi_v; ++i) m |= 1u << (L[i] - lo_v);
+    P.bits[(long long)b * words + w] = m;
+  }
 }
 
-__global__ void union_scatter_kernel(UnionArgs a) {
+// The union bitmap: the OR of the B row bitmaps, word by word.
+__global__ void union_or_kernel(UnionArgs a) {
   const UnionProb& P = blockIdx.y == 0 ? a.p[0] : a.p[1];
   const int words = (P.n + 31) / 32;
-  const long long total = (long long)a.B * P.k;
-  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < total; e += (long long)gridDim.x * blockDim.x) {
-    const int b = (int)(e / P.k);
-    const int j = P.idx[(long long)b * P.idx_bstride + (e - (long long)b * P.k)];
-    if ((unsigned)j >= (unsigned)P.n) continue;   // out-of-range entries select nothing
-    const unsigned m = 1u << (j & 31);
-    atomicOr(&P.bits[(long long)b * words + (j >> 5)], m);
-    atomicOr(&P.bits[(long long)a.B * words + (j >> 5)], m);
+  for (int w = blockIdx.x * blockDim.x + threadIdx.x; w < words; w += gridDim.x * blockDim.x) {
+    unsigned m = 0u;
+    for (int b = 0; b < a.B; ++b) m |= P.bits[(long long)b * words + w];
+    P.bits[(long long)a.B * words + w] = m;
   }
 }
 
@@ -467,12 +482,12 @@ __global__ void heads_to_union_kernel(const float* o, int kh, int dh, const int3
 hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
   for (int i = 0; i < a.nprob; ++i)
     if (a.p[i].n > kUnionMaxN || a.p[i].n <= 0) return hipErrorInvalidValue;
-  int maxk = 1;
-  for (int i = 0; i < a.nprob; ++i) maxk = max(maxk, a.p[i].k);
-  hipLaunchKernelGGL(union_zero_kernel, dim3(64, a.nprob), dim3(256), 0, s, a);
-  const long long ent = (long long)a.B * maxk;
-  const int sb = (int)std::min<long long>(1024, (ent + 255) / 256);
-  hipLaunchKernelGGL(union_scatter_kernel, dim3(sb, a.nprob), dim3(256), 0, s, a);
+  int maxw = 1;
+  for (int i = 0; i < a.nprob; ++i) maxw = max(maxw, (a.p[i].n + 31) / 32);
+  const long long rows_words = (long long)a.B * maxw;
+  hipLaunchKernelGGL(union_rows_kernel, dim3((unsigned)std::min<long long>(1024, (rows_words + 255) / 256), a.nprob),
+                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL(union_or_kernel, dim3((maxw + 255) / 256, a.nprob), dim3(256), 0, s, a);
   hipLaunchKernelGGL(union_list_kernel, dim3(a.nprob), dim3(kUnionBlock), 0, s, a);
   return hipGetLastError();
 }
