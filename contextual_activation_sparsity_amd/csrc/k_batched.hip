@@ -5,9 +5,9 @@
 // row); the union only shares the weight traffic: every selected weight row is read once
 // and multiplied against all B activation rows on the matrix cores.
 //
-//  * union_rows / union_or / union_list: per-row bitmaps of the selected groups (neurons or
-//    heads, from the rows' ascending lists by binary search, no atomics), their OR, and the OR
-//    as an ascending list with its length in device memory.
+//  * union_rows / union_list: per-row bitmaps of the selected groups (neurons or heads, from
+//    the rows' ascending lists by binary search, no atomics), then their OR and the OR as an
+//    ascending list with its length in device memory.
 //  * rows_norm_f16: RMSNorm of each row, rounded to fp16 (the MFMA operand type).
 //  * gemm_rows (up-projection, q/k/v and W1; both predictor factors): out[b][i] =
 //    act(W[row_i] . X[b] + bias), masked per row. A block stages 64 gathered weight rows and
@@ -68,32 +68,26 @@ __global__ void union_rows_kernel(UnionArgs a) {
   }
 }
 
-// The union bitmap: the OR of the B row bitmaps, word by word.
-__global__ void union_or_kernel(UnionArgs a) {
-  const UnionProb& P = blockIdx.y == 0 ? a.p[0] : a.p[1];
-  const int words = (P.n + 31) / 32;
-  for (int w = blockIdx.x * blockDim.x + threadIdx.x; w < words; w += gridDim.x * blockDim.x) {
-    unsigned m = 0u;
-    for (int b = 0; b < a.B; ++b) m |= P.bits[(long long)b * words + w];
-    P.bits[(long long)a.B * words + w] = m;
-  }
-}
-
 constexpr int kUnionBlock = 1024;
-// One block per problem: union bitmap -> ascending list + its length.
+// One block per problem: the OR of the row bitmaps (kept as row B) -> ascending list + its length.
 __global__ __launch_bounds__(kUnionBlock) void union_list_kernel(UnionArgs a) {
   __shared__ unsigned s_scan[kUnionBlock / kWave];
   const UnionProb& P = blockIdx.x == 0 ? a.p[0] : a.p[1];
   const int words = (P.n + 31) / 32;
-  const unsigned* ub = P.bits + (long long)a.B * words;
+  unsigned* ub = P.bits + (long long)a.B * words;   // the union bitmap (row B)
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
   constexpr int WPT = kUnionMaxN / 32 / kUnionBlock;   // words per thread
   unsigned m[WPT];
   unsigned cnt = 0;
 #pragma unroll
-  for (int q = 0; q < WPT; ++q) {
+  for (int q = 0; q < WPT; ++q) {   // OR of the row bitmaps, word by word
     const int wi = tid * WPT + q;
-    m[q] = wi < words ? ub[wi] : 0u;
+    unsigned u = 0u;
+    if (wi < words) {
+      for (int b = 0; b < a.B; ++b) u |= P.bits[(long long)b * words + wi];
+      ub[wi] = u;
+    }
+    m[q] = u;
     cnt += __popc(m[q]);
   }
   unsigned incl = cnt;
@@ -487,7 +481,6 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
   const long long rows_words = (long long)a.B * maxw;
   hipLaunchKernelGGL(union_rows_kernel, dim3((unsigned)std::min<long long>(1024, (rows_words + 255) / 256), a.nprob),
                      dim3(256), 0, s, a);
-  hipLaunchKernelGGL(union_or_kernel, dim3((maxw + 255) / 256, a.nprob), dim3(256), 0, s, a);
   hipLaunchKernelGGL(union_list_kernel, dim3(a.nprob), dim3(kUnionBlock), 0, s, a);
   return hipGetLastError();
 }
