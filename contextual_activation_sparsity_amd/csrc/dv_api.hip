@@ -47,17 +47,25 @@ struct DeviceInfo {
   hipEvent_t ev_in = nullptr, ev_sel[2] = {nullptr, nullptr};
 };
 std::mutex g_mu;
-std::map<int, DeviceInfo> g_dev;
+std::map<int, int> g_cus;                  // compute units per device
+thread_local std::map<int, DeviceInfo> t_dev;   // the stack's fork/join events: per device and thread
 
+// Compute units of the current device and, with events, this thread's stack events on it.
+// Events are per thread so that stack calls from different host threads never record or
+// wait on each other's events.
 dv_status device_info(DeviceInfo** out, bool events) {
   int dev = 0;
   DV_HIP(hipGetDevice(&dev));
-  std::lock_guard<std::mutex> lk(g_mu);
-  DeviceInfo& di = g_dev[dev];
+  DeviceInfo& di = t_dev[dev];
   if (di.cus == 0) {
-    int cus = 0;
-    DV_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-    di.cus = cus > 0 ? cus : 1;
+    std::lock_guard<std::mutex> lk(g_mu);
+    int& cus = g_cus[dev];
+    if (cus == 0) {
+      int n = 0;
+      DV_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev));
+      cus = n > 0 ? n : 1;
+    }
+    di.cus = cus;
   }
   if (events && di.ev_in == nullptr) {
     DV_HIP(hipEventCreateWithFlags(&di.ev_in, hipEventDisableTiming));

@@ -130,3 +130,37 @@ def test_device_generator_matches_host(dv):
         sdev.fill_(part, key, sg, start=17 * 37)
         torch.cuda.synchronize()
         assert np.array_equal(part.cpu().numpy(), host[17:22])
+
+
+def test_stack_from_two_host_threads(dv):
+    """Two host threads run the stack at the same time on their own stream pairs (each with
+    its own caches and workspace): the stack's fork/join events are per thread, so every
+    run gives the bits of the single-threaded run."""
+    import threading
+    w = W_RAG16
+    n = 3
+    host, dev, kcs, vcs = build_stack(w, n)
+    xs = [synth.x_input(w, step=s) for s in (4, 5)]
+    ref = [run_stack(dv, w, dev, kcs, vcs, x, two_streams=True) for x in xs]
+    out = [[None] * 3 for _ in xs]
+    err = []
+
+    def worker(t):
+        try:
+            main = torch.cuda.Stream()
+            with torch.cuda.stream(main):
+                for rep in range(3):
+                    out[t][rep] = run_stack(dv, w, dev, kcs, vcs, xs[t], two_streams=True)
+        except Exception as e:  # reported below, on the test's thread
+            err.append(e)
+
+    th = [threading.Thread(target=worker, args=(t,)) for t in range(len(xs))]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not err, err
+    for t in range(len(xs)):
+        for rep in range(3):
+            for a, b in zip(out[t][rep], ref[t]):
+                assert np.array_equal(a, b), f"thread {t} run {rep} differs from the single-threaded run"
