@@ -47,25 +47,50 @@ __device__ __forceinline__ int rank_below(const unsigned* bits, int j) {
 // Row bitmaps without atomics: thread (row b, word w) finds the first entry >= 32w of the row's
 // ascending list by binary search and sets the bits of the entries below 32(w+1) (entries
 // outside [0, n) select nothing). Every word is written whole, so no clearing pass is needed.
-__global__ void union_rows_kernel(UnionArgs a) {
-  const UnionProb& P = blockIdx.y == 0 ? a.p[0] : a.p[1];
+constexpr int kUnionRowsBlock = 256;    // bitmap words per block
+constexpr int kUnionRowsLds = 16384;    // a row's list is searched in LDS up to this length
+constexpr int kUnionRowsLdsPT = 16;     // list entries each thread stages per sweep
+__global__ __launch_bounds__(kUnionRowsBlock) void union_rows_kernel(UnionArgs a) {
+  __shared__ int32_t s_l[kUnionRowsLds];
+  const UnionProb& P = blockIdx.z == 0 ? a.p[0] : a.p[1];
+  const int tid = threadIdx.x;
   const int words = (P.n + 31) / 32;
-  const long long total = (long long)a.B * words;
-  for (long long t = blockIdx.x * (long long)blockDim.x + threadIdx.x; t < total;
-       t += (long long)gridDim.x * blockDim.x) {
-    const int b = (int)(t / words), w = (int)(t - (long long)b * words);
-    const int32_t* L = P.idx + (long long)b * P.idx_bstride;
-    const int lo_v = 32 * w, hi_v = min(32 * w + 32, P.n);
-    int lo = 0, hi = P.k;   // first position with L[pos] >= lo_v
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (L[mid] < lo_v) lo = mid + 1;
-      else hi = mid;
+  const int b = blockIdx.y;
+  const int w0 = blockIdx.x * kUnionRowsBlock;
+  if (w0 >= words) return;   // block-uniform: the other problem may have more words
+  const int32_t* L = P.idx + (long long)b * P.idx_bstride;
+  // Row b's ascending list, staged in LDS with every load of a sweep in flight together, so
+  // the searches below wait on LDS instead of on a chain of dependent global loads.
+  const bool lds = P.k <= kUnionRowsLds;   // block-uniform
+  if (lds) {
+    for (int i0 = 0; i0 < P.k; i0 += kUnionRowsBlock * kUnionRowsLdsPT) {
+      int32_t v[kUnionRowsLdsPT];
+#pragma unroll
+      for (int q = 0; q < kUnionRowsLdsPT; ++q) {
+        const int i = i0 + q * kUnionRowsBlock + tid;
+        v[q] = i < P.k ? L[i] : 0;
+      }
+#pragma unroll
+      for (int q = 0; q < kUnionRowsLdsPT; ++q) {
+        const int i = i0 + q * kUnionRowsBlock + tid;
+        if (i < P.k) s_l[i] = v[q];
+      }
     }
-    unsigned m = 0u;
-    for (int i = lo; i < P.k && L[i] < hi_v; ++i) m |= 1u << (L[i] - lo_v);
-    P.bits[(long long)b * words + w] = m;
+    __syncthreads();
   }
+  const int w = w0 + tid;
+  if (w >= words) return;
+  auto at = [&](int i) -> int32_t { return lds ? s_l[i] : L[i]; };
+  const int lo_v = 32 * w, hi_v = min(32 * w + 32, P.n);
+  int lo = 0, hi = P.k;   // first position with L[pos] >= lo_v
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (at(mid) < lo_v) lo = mid + 1;
+    else hi = mid;
+  }
+  unsigned m = 0u;
+  for (int i = lo; i < P.k && at(i) < hi_v; ++i) m |= 1u << (at(i) - lo_v);
+  P.bits[(long long)b * words + w] = m;
 }
 
 constexpr int kUnionBlock = 1024;
@@ -84,7 +109,11 @@ __global__ __launch_bounds__(kUnionBlock) void union_list_kernel(UnionArgs a) {
     const int wi = tid * WPT + q;
     unsigned u = 0u;
     if (wi < words) {
-      for (int b = 0; b < a.B; ++b) u |= P.bits[(long long)b * words + wi];
+      unsigned r[kBatchMax];   // every row's word in flight together
+#pragma unroll
+      for (int b = 0; b < kBatchMax; ++b) r[b] = b < a.B ? P.bits[(long long)b * words + wi] : 0u;
+#pragma unroll
+      for (int b = 0; b < kBatchMax; ++b) u |= r[b];
       ub[wi] = u;
     }
     m[q] = u;
@@ -478,9 +507,8 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
     if (a.p[i].n > kUnionMaxN || a.p[i].n <= 0) return hipErrorInvalidValue;
   int maxw = 1;
   for (int i = 0; i < a.nprob; ++i) maxw = max(maxw, (a.p[i].n + 31) / 32);
-  const long long rows_words = (long long)a.B * maxw;
-  hipLaunchKernelGGL(union_rows_kernel, dim3((unsigned)std::min<long long>(1024, (rows_words + 255) / 256), a.nprob),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL(union_rows_kernel, dim3((maxw + kUnionRowsBlock - 1) / kUnionRowsBlock, a.B, a.nprob),
+                     dim3(kUnionRowsBlock), 0, s, a);
   hipLaunchKernelGGL(union_list_kernel, dim3(a.nprob), dim3(kUnionBlock), 0, s, a);
   return hipGetLastError();
 }
