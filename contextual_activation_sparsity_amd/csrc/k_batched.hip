@@ -344,8 +344,13 @@ __global__ void gemm_rows_finish_kernel(GemmRowsArgs a) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int b = blockIdx.y;
   if (i >= nrows) return;
+  float p[kRowsMaxSplit];   // every slice's partial in flight together, summed in slice order
+#pragma unroll
+  for (int q = 0; q < kRowsMaxSplit; ++q) p[q] = q < a.ksplit ? a.kpart[((long long)q * a.B + b) * a.kld + i] : 0.f;
   float v = 0.f;
-  for (int q = 0; q < a.ksplit; ++q) v += a.kpart[((long long)q * a.B + b) * a.kld + i];
+#pragma unroll
+  for (int q = 0; q < kRowsMaxSplit; ++q)
+    if (q < a.ksplit) v += p[q];
   rows_store(a, i, b, v);
 }
 
