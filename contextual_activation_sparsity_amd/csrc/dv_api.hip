@@ -138,7 +138,7 @@ dv_status check_pred(const dv_predictor* P) {
 struct Layout {
   size_t z, s_mlp, s_head, idx, heads, qkv, apart, o, h1, u, part, tk_mlp, tk_head, kpart, total;
   // batched path (B >= 2): union bitmaps and lists, fp16 operands
-  size_t ubits, hbits, ulist, uhlist, counts, xh, xl, zh, zl, cu, co;
+  size_t ubits, hbits, ulist, uhlist, counts, ucnt, xh, xl, zh, zl, cu, co;
   int max_u, max_uh;
   int max_chunks;
 };
@@ -174,6 +174,7 @@ Layout layout_of(const dv_dims* d, int B, int k, int kh) {
     L.ulist = take(4 * (size_t)d->d_ffn);
     L.uhlist = take(4 * (size_t)d->n_heads);
     L.counts = take(4 * 4);
+    L.ucnt = take(4 * 2 * (size_t)(dv::kUnionMaxN / 32 / dv::kUnionWpb));
     L.xh = take(2 * Bz * d->d_model);
     L.xl = take(2 * Bz * d->d_model);
     L.zh = take(2 * Bz * (d->rank_mlp + d->rank_head));
@@ -414,9 +415,13 @@ dv_status run_union(const dv_dims* d, int B, const int32_t* idx, int k, const in
   dv::UnionArgs u{};
   u.B = B;
   int* counts = at<int>(ws, L.counts);
-  if (idx != nullptr) u.p[u.nprob++] = {idx, k, d->d_ffn, k, at<unsigned>(ws, L.ubits), at<int32_t>(ws, L.ulist), counts};
+  unsigned* bcnt = at<unsigned>(ws, L.ucnt);
+  constexpr int nb = dv::kUnionMaxN / 32 / dv::kUnionWpb;
+  if (idx != nullptr)
+    u.p[u.nprob++] = {idx, k, d->d_ffn, k, at<unsigned>(ws, L.ubits), at<int32_t>(ws, L.ulist), counts, bcnt};
   if (heads != nullptr)
-    u.p[u.nprob++] = {heads, kh, d->n_heads, kh, at<unsigned>(ws, L.hbits), at<int32_t>(ws, L.uhlist), counts + 1};
+    u.p[u.nprob++] = {heads, kh, d->n_heads, kh, at<unsigned>(ws, L.hbits), at<int32_t>(ws, L.uhlist), counts + 1,
+                      bcnt + nb};
   if (u.nprob == 0) return DV_OK;
   if (u.nprob == 1) u.p[1] = u.p[0];
   DV_HIP(dv::launch_union(u, st));

@@ -135,6 +135,7 @@ hipError_t launch_topk(const TopkArgs& a, int B, hipStream_t s);
 constexpr int kUnionMaxN = 65536;    // groups (neurons or heads) per problem
 constexpr int kBatchMax = 32;        // rows per batched launch
 constexpr int kBatchMaxRG = 32;      // row groups of the down-projection
+constexpr int kUnionWpb = 64;        // bitmap words per block of the union's OR and list
 struct UnionProb {
   const int32_t* idx;       // [B][idx_bstride]: the row's k selected groups (ascending)
   long long idx_bstride;
@@ -143,6 +144,7 @@ struct UnionProb {
   unsigned* bits;           // [B + 1][ceil(n/32)]: row bitmaps, then their OR
   int32_t* list;            // [n]: the OR as an ascending list
   int* count;               // its length
+  unsigned* bcnt;           // [kUnionMaxN / 32 / kUnionWpb] scratch: set bits per block of words
 };
 struct UnionArgs {
   UnionProb p[2];

@@ -5,9 +5,10 @@
 // row); the union only shares the weight traffic: every selected weight row is read once
 // and multiplied against all B activation rows on the matrix cores.
 //
-//  * union_rows / union_list: per-row bitmaps of the selected groups (neurons or heads, from
-//    the rows' ascending lists by binary search, no atomics), then their OR and the OR as an
-//    ascending list with its length in device memory.
+//  * union_rows / union_or / union_list: per-row bitmaps of the selected groups (neurons or
+//    heads, from the rows' ascending lists by binary search in LDS, no atomics), then their
+//    OR with a count per block of words, then the OR as an ascending list (each block starts
+//    at the counts of the blocks before it) with its length in device memory.
 //  * rows_norm_f16: RMSNorm of each row, rounded to fp16 (the MFMA operand type).
 //  * gemm_rows (up-projection, q/k/v and W1; both predictor factors): out[b][i] =
 //    act(W[row_i] . X[b] + bias), masked per row. A block stages 64 gathered weight rows and
@@ -93,57 +94,75 @@ __global__ __launch_bounds__(kUnionRowsBlock) void union_rows_kernel(UnionArgs a
   P.bits[(long long)b * words + w] = m;
 }
 
-constexpr int kUnionBlock = 1024;
-// One block per problem: the OR of the row bitmaps (kept as row B) -> ascending list + its length.
-__global__ __launch_bounds__(kUnionBlock) void union_list_kernel(UnionArgs a) {
-  __shared__ unsigned s_scan[kUnionBlock / kWave];
-  const UnionProb& P = blockIdx.x == 0 ? a.p[0] : a.p[1];
+// OR of the row bitmaps (kept as row B), kUnionWpb words per block: four groups of eight rows
+// per word with every load in flight, then the set bits of the block's words.
+constexpr int kUnionOrBlock = 4 * kUnionWpb;
+static_assert(kBatchMax <= 32, "four groups of eight rows cover a batch");
+__global__ __launch_bounds__(kUnionOrBlock) void union_or_kernel(UnionArgs a) {
+  __shared__ unsigned s_or[4][kUnionWpb];
+  const UnionProb& P = blockIdx.y == 0 ? a.p[0] : a.p[1];
   const int words = (P.n + 31) / 32;
-  unsigned* ub = P.bits + (long long)a.B * words;   // the union bitmap (row B)
-  const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-  constexpr int WPT = kUnionMaxN / 32 / kUnionBlock;   // words per thread
-  unsigned m[WPT];
-  unsigned cnt = 0;
+  const int w0 = blockIdx.x * kUnionWpb;
+  if (w0 >= words) return;   // block-uniform: the other problem may have more words
+  const int tid = threadIdx.x, wl = tid % kUnionWpb, rg = tid / kUnionWpb;
+  const int w = w0 + wl;
+  unsigned r[8];
 #pragma unroll
-  for (int q = 0; q < WPT; ++q) {   // OR of the row bitmaps, word by word
-    const int wi = tid * WPT + q;
-    unsigned u = 0u;
-    if (wi < words) {
-      unsigned r[kBatchMax];   // every row's word in flight together
-#pragma unroll
-      for (int b = 0; b < kBatchMax; ++b) r[b] = b < a.B ? P.bits[(long long)b * words + wi] : 0u;
-#pragma unroll
-      for (int b = 0; b < kBatchMax; ++b) u |= r[b];
-      ub[wi] = u;
-    }
-    m[q] = u;
-    cnt += __popc(m[q]);
+  for (int q = 0; q < 8; ++q) {
+    const int b = 8 * rg + q;
+    r[q] = (w < words && b < a.B) ? P.bits[(long long)b * words + w] : 0u;
   }
-  unsigned incl = cnt;
+  unsigned u = 0u;
 #pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const unsigned t = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += t;
-  }
-  if (lane == kWave - 1) s_scan[w] = incl;
+  for (int q = 0; q < 8; ++q) u |= r[q];
+  s_or[rg][wl] = u;
   __syncthreads();
-  unsigned before = 0, total = 0;
-  for (int i = 0; i < kUnionBlock / kWave; ++i) {
-    if (i < w) before += s_scan[i];
-    total += s_scan[i];
-  }
-  unsigned pos = before + incl - cnt;
+  if (tid < kUnionWpb) {   // wave 0: one word per lane
+    const unsigned v = s_or[0][tid] | s_or[1][tid] | s_or[2][tid] | s_or[3][tid];
+    if (w < words) P.bits[(long long)a.B * words + w] = v;
+    unsigned c = (unsigned)__popc(v);
 #pragma unroll
-  for (int q = 0; q < WPT; ++q) {
-    unsigned mm = m[q];
-    const int base = (tid * WPT + q) * 32;
-    while (mm != 0u) {
-      const int bit = __builtin_ctz(mm);
-      mm &= mm - 1u;
-      P.list[pos++] = base + bit;
-    }
+    for (int off = kWave / 2; off > 0; off >>= 1) c += __shfl_xor(c, off, kWave);
+    if (tid == 0) P.bcnt[blockIdx.x] = c;
   }
-  if (tid == 0) *P.count = (int)total;
+}
+static_assert(kUnionWpb == kWave, "the list kernel is one wave per block of words");
+
+// The OR as an ascending list: block x (one wave, one word per lane) starts at the set bits of
+// the blocks before it, scans its words' counts, stages its part of the list in LDS and
+// writes it with coalesced stores; the last block writes the list's length.
+__global__ __launch_bounds__(kUnionWpb) void union_list_kernel(UnionArgs a) {
+  __shared__ int32_t s_l[kUnionWpb * 32];
+  const UnionProb& P = blockIdx.y == 0 ? a.p[0] : a.p[1];
+  const int words = (P.n + 31) / 32;
+  const int nblk = (words + kUnionWpb - 1) / kUnionWpb;
+  const int x = blockIdx.x;
+  if (x >= nblk) return;   // block-uniform
+  const int lane = threadIdx.x;
+  static_assert(kUnionMaxN / 32 / kUnionWpb <= kWave, "one lane per earlier block");
+  unsigned off = lane < x ? P.bcnt[lane] : 0u;
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) off += __shfl_xor(off, o, kWave);
+  const int w = x * kUnionWpb + lane;
+  const unsigned v = w < words ? P.bits[(long long)a.B * words + w] : 0u;
+  const unsigned pc = (unsigned)__popc(v);
+  unsigned incl = pc;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const unsigned t = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += t;
+  }
+  const unsigned tot = __shfl(incl, kWave - 1, kWave);
+  unsigned p = incl - pc;
+  unsigned m = v;
+  while (m != 0u) {
+    const int bit = __builtin_ctz(m);
+    m &= m - 1u;
+    s_l[p++] = w * 32 + bit;
+  }
+  __syncthreads();
+  for (unsigned i = lane; i < tot; i += kUnionWpb) P.list[off + i] = s_l[i];
+  if (x == nblk - 1 && lane == 0) *P.count = (int)(off + tot);
 }
 
 // ---------------------------------------------------------------------------
@@ -514,7 +533,9 @@ hipError_t launch_union(const UnionArgs& a, hipStream_t s) {
   for (int i = 0; i < a.nprob; ++i) maxw = max(maxw, (a.p[i].n + 31) / 32);
   hipLaunchKernelGGL(union_rows_kernel, dim3((maxw + kUnionRowsBlock - 1) / kUnionRowsBlock, a.B, a.nprob),
                      dim3(kUnionRowsBlock), 0, s, a);
-  hipLaunchKernelGGL(union_list_kernel, dim3(a.nprob), dim3(kUnionBlock), 0, s, a);
+  const int nblk = (maxw + kUnionWpb - 1) / kUnionWpb;
+  hipLaunchKernelGGL(union_or_kernel, dim3(nblk, a.nprob), dim3(kUnionOrBlock), 0, s, a);
+  hipLaunchKernelGGL(union_list_kernel, dim3(nblk, a.nprob), dim3(kUnionWpb), 0, s, a);
   return hipGetLastError();
 }
 
