@@ -278,12 +278,12 @@ dv_status run_predict_batched(const dv_dims* d, const dv_predictor* P, const flo
   _Float16* zh = at<_Float16>(ws, L.zh);
   _Float16* zl = at<_Float16>(ws, L.zl);
   DV_HIP(dv::launch_rows_norm_f16(x, D, nullptr, D, 0.f, B, xh, xl, D, st));
-  dv::GemmRowsArgs a = rows_args(P->p1_mlp, D, D, nullptr, nullptr, 1, rm, B, xh, D, at<float>(ws, L.kpart));
+  // both stage-1 factors in one launch: rows [0, rm) of P1_mlp, then rows of P1_head (z = [z_m; z_h])
+  dv::GemmRowsArgs a = rows_args(P->p1_mlp, D, D, nullptr, nullptr, 1, rm + rh, B, xh, D, at<float>(ws, L.kpart));
+  a.W_b = P->p1_head; a.n_rows_a = rm;
   a.X_lo = xl; a.mode = dv::kGemmOutF16; a.outh = zh; a.outh_lo = zl; a.ldo = rm + rh;
-  DV_HIP(dv::launch_gemm_rows(a, rm, cus, st));
-  a = rows_args(P->p1_head, D, D, nullptr, nullptr, 1, rh, B, xh, D, at<float>(ws, L.kpart));
-  a.X_lo = xl; a.mode = dv::kGemmOutF16; a.outh = zh + rm; a.outh_lo = zl + rm; a.ldo = rm + rh;
-  DV_HIP(dv::launch_gemm_rows(a, rh, cus, st));
+  DV_HIP(dv::launch_gemm_rows(a, rm + rh, cus, st));
+  a.W_b = nullptr; a.n_rows_a = 0;
   a = rows_args(P->p2_mlp, rm, rm, nullptr, nullptr, 1, d->d_ffn, B, zh, rm + rh, at<float>(ws, L.kpart));
   a.X_lo = zl; a.mode = dv::kGemmOutF32; a.outf = s_mlp; a.ldo = d->d_ffn;
   DV_HIP(dv::launch_gemm_rows(a, d->d_ffn, cus, st));

@@ -183,6 +183,8 @@ struct GemmRowsArgs {                // out[b][i] = act(W[row_i] . X[b] + bias[r
   float* kpart;                      // nullable: [kRowsMaxSplit][B][kld] partial sums when K is split over blocks
   long long kld;
   int ksplit;                        // set by the launcher
+  const void* W_b;                   // nullable: rows i >= n_rows_a are row i - n_rows_a of W_b (same ld;
+  int n_rows_a;                      //   G = 1 and no sel), so two matrices on one input share a launch
 };
 constexpr int kRowsMaxSplit = 32;       // K slices of a short up-projection
 constexpr int kRowsSplitMaxRows = 4096; // only launches of at most this many rows split K

@@ -289,8 +289,13 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
       const int grp = a.sel ? a.sel[g] : g;
       if ((unsigned)grp < (unsigned)a.n_groups) wrow = (long long)grp * a.G + (i - g * a.G);
     }
+    const half_t* base = W;
+    if (a.W_b != nullptr && wrow >= a.n_rows_a) {   // second matrix of a two-matrix launch
+      base = reinterpret_cast<const half_t*>(a.W_b);
+      wrow -= a.n_rows_a;
+    }
     wok[q] = wrow >= 0;
-    wp[q] = W + (wrow >= 0 ? wrow : 0) * a.ld + kk;
+    wp[q] = base + (wrow >= 0 ? wrow : 0) * a.ld + kk;
   }
   u32x4 wreg[8];
   h8v xreg[XL][XLD];
@@ -556,6 +561,8 @@ static void launch_rows_lds(const GemmRowsArgs& a, int max_rows, int ks, hipStre
 hipError_t launch_gemm_rows(const GemmRowsArgs& a_in, int max_rows, int cus, hipStream_t s) {
   GemmRowsArgs a = a_in;
   if (a.d % 8 != 0 || a.B < 1 || a.B > kBatchMax || max_rows < 0) return hipErrorInvalidValue;   // tail K steps are guarded
+  if (a.W_b != nullptr && (a.G != 1 || a.sel != nullptr || a.n_rows_a < 0 || a.n_rows_a > a.n_groups))
+    return hipErrorInvalidValue;
   if (max_rows == 0) return hipSuccess;
   const bool split = a.X_lo != nullptr;
   const int tiles = (max_rows + 63) / 64;
