@@ -286,6 +286,14 @@ dv_status run_predict_batched(const dv_dims* d, const dv_predictor* P, const flo
   a.W_b = nullptr; a.n_rows_a = 0;
   a = rows_args(P->p2_mlp, rm, rm, nullptr, nullptr, 1, d->d_ffn, B, zh, rm + rh, at<float>(ws, L.kpart));
   a.X_lo = zl; a.mode = dv::kGemmOutF32; a.outf = s_mlp; a.ldo = d->d_ffn;
+  if (rm == rh && d->d_ffn % 64 == 0) {
+    // the head scores' rows ride in the neuron scores' launch (their own input z_h and output)
+    a.n_groups = d->d_ffn + d->n_heads;
+    a.W_b = P->p2_head; a.n_rows_a = d->d_ffn; a.X_b = zh + rm; a.X_lo_b = zl + rm;
+    a.outf_b = s_head; a.ldo_b = d->n_heads;
+    DV_HIP(dv::launch_gemm_rows(a, d->d_ffn + d->n_heads, cus, st));
+    return DV_OK;
+  }
   DV_HIP(dv::launch_gemm_rows(a, d->d_ffn, cus, st));
   a = rows_args(P->p2_head, rh, rh, nullptr, nullptr, 1, d->n_heads, B, zh + rm, rm + rh, at<float>(ws, L.kpart));
   a.X_lo = zl + rm; a.mode = dv::kGemmOutF32; a.outf = s_head; a.ldo = d->n_heads;

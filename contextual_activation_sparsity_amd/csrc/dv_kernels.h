@@ -184,7 +184,11 @@ struct GemmRowsArgs {                // out[b][i] = act(W[row_i] . X[b] + bias[r
   long long kld;
   int ksplit;                        // set by the launcher
   const void* W_b;                   // nullable: rows i >= n_rows_a are row i - n_rows_a of W_b (same ld;
-  int n_rows_a;                      //   G = 1 and no sel), so two matrices on one input share a launch
+  int n_rows_a;                      //   G = 1 and no sel), so two matrices share a launch
+  const _Float16* X_b;               // nullable: activations (and X_lo_b remainders) of W_b's rows; then
+  const _Float16* X_lo_b;            //   n_rows_a is a multiple of 64, so a block's rows use one input
+  float* outf_b;                     // nullable (kGemmOutF32): outputs of W_b's rows, [B][ldo_b]
+  long long ldo_b;
 };
 constexpr int kRowsMaxSplit = 32;       // K slices of a short up-projection
 constexpr int kRowsSplitMaxRows = 4096; // only launches of at most this many rows split K

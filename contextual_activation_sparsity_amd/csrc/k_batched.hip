@@ -247,7 +247,8 @@ __device__ __forceinline__ void rows_store(const GemmRowsArgs& a, int i, int b, 
     a.outh[(long long)b * a.ldo + i] = hi;
     if (a.outh_lo) a.outh_lo[(long long)b * a.ldo + i] = static_cast<_Float16>(vv - static_cast<float>(hi));
   } else if (a.mode == kGemmOutF32) {
-    a.outf[(long long)b * a.ldo + i] = on ? v : 0.f;
+    if (a.outf_b != nullptr && i >= a.n_rows_a) a.outf_b[(long long)b * a.ldo_b + (i - a.n_rows_a)] = on ? v : 0.f;
+    else a.outf[(long long)b * a.ldo + i] = on ? v : 0.f;
   } else if (on && rb != nullptr) {   // q/k/v into the row's own slot order
     const int slot = rank_below(rb, grp);
     a.outf[((long long)b * a.kh + slot) * a.G + wi] = v;
@@ -297,6 +298,10 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
     wok[q] = wrow >= 0;
     wp[q] = base + (wrow >= 0 ? wrow : 0) * a.ld + kk;
   }
+  // A block's 64 rows all belong to one matrix of a two-matrix launch, hence to one input.
+  const bool second = a.X_b != nullptr && r0 >= a.n_rows_a;
+  const _Float16* Xs = second ? a.X_b : a.X;
+  const _Float16* XLs = second ? a.X_lo_b : a.X_lo;
   u32x4 wreg[8];
   h8v xreg[XL][XLD];
   auto load = [&](int k0) {
@@ -309,9 +314,9 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
     for (int p = 0; p < XLD; ++p) {
       const int b = lrow + 8 * p;
       const bool ok = kok && b < a.B;
-      xreg[0][p] = ok ? *reinterpret_cast<const h8v*>(a.X + (long long)b * a.ldx + k0 + kk) : h8v{0, 0, 0, 0, 0, 0, 0, 0};
+      xreg[0][p] = ok ? *reinterpret_cast<const h8v*>(Xs + (long long)b * a.ldx + k0 + kk) : h8v{0, 0, 0, 0, 0, 0, 0, 0};
       if constexpr (SPLIT)
-        xreg[1][p] = ok ? *reinterpret_cast<const h8v*>(a.X_lo + (long long)b * a.ldx + k0 + kk)
+        xreg[1][p] = ok ? *reinterpret_cast<const h8v*>(XLs + (long long)b * a.ldx + k0 + kk)
                         : h8v{0, 0, 0, 0, 0, 0, 0, 0};
     }
   };
@@ -562,6 +567,8 @@ hipError_t launch_gemm_rows(const GemmRowsArgs& a_in, int max_rows, int cus, hip
   GemmRowsArgs a = a_in;
   if (a.d % 8 != 0 || a.B < 1 || a.B > kBatchMax || max_rows < 0) return hipErrorInvalidValue;   // tail K steps are guarded
   if (a.W_b != nullptr && (a.G != 1 || a.sel != nullptr || a.n_rows_a < 0 || a.n_rows_a > a.n_groups))
+    return hipErrorInvalidValue;
+  if (a.X_b != nullptr && (a.W_b == nullptr || a.n_rows_a % 64 != 0 || (a.X_lo != nullptr) != (a.X_lo_b != nullptr)))
     return hipErrorInvalidValue;
   if (max_rows == 0) return hipSuccess;
   const bool split = a.X_lo != nullptr;
