@@ -177,6 +177,44 @@ __global__ __launch_bounds__(kNormBlock) void rows_norm_f16_kernel(const float* 
   __shared__ float s_red[kNormBlock / kWave];
   const int b = blockIdx.x, tid = threadIdx.x;
   const float* xb = x + (long long)b * ldx;
+  _Float16* ob = out + (long long)b * ldo;
+  _Float16* lb = out_lo ? out_lo + (long long)b * ldo : nullptr;
+  if (d <= kNormBlock * 4 * kNormPT) {
+    // One sweep: the row and its gains are loaded together and kept in registers.
+    f32x4 t[kNormPT], gg[kNormPT];
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < kNormPT; ++q) {
+      const int c = (q * kNormBlock + tid) * 4;
+      const bool ok = c < d;
+      t[q] = ok ? *reinterpret_cast<const f32x4*>(xb + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+      gg[q] = (ok && g) ? *reinterpret_cast<const f32x4*>(g + c) : f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+#pragma unroll
+    for (int q = 0; q < kNormPT; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ss = fmaf(t[q][e], t[q][e], ss);
+    ss = group_sum<kWave>(ss);
+    if (tid % kWave == 0) s_red[tid / kWave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < kNormBlock / kWave; ++i) tot += s_red[i];
+    const float inv = g ? 1.0f / sqrtf(tot / (float)d + eps) : 1.0f;   // no gain: plain cast
+#pragma unroll
+    for (int q = 0; q < kNormPT; ++q) {
+      const int c = (q * kNormBlock + tid) * 4;
+      if (c >= d) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = t[q][e] * inv * gg[q][e];
+        const _Float16 hi = static_cast<_Float16>(v);
+        ob[c + e] = hi;
+        if (lb) lb[c + e] = static_cast<_Float16>(v - static_cast<float>(hi));
+      }
+    }
+    return;
+  }
   float ss = 0.f;
   for (int c0 = 0; c0 < d; c0 += kNormBlock * 4 * kNormPT) {
     f32x4 t[kNormPT];
@@ -197,8 +235,6 @@ __global__ __launch_bounds__(kNormBlock) void rows_norm_f16_kernel(const float* 
 #pragma unroll
   for (int i = 0; i < kNormBlock / kWave; ++i) tot += s_red[i];
   const float inv = g ? 1.0f / sqrtf(tot / (float)d + eps) : 1.0f;   // no gain: plain cast
-  _Float16* ob = out + (long long)b * ldo;
-  _Float16* lb = out_lo ? out_lo + (long long)b * ldo : nullptr;
   for (int c0 = 0; c0 < d; c0 += kNormBlock * 4 * kNormPT) {
     f32x4 t[kNormPT], gg[kNormPT];
 #pragma unroll
