@@ -14,6 +14,8 @@
 //     holding the k-th largest key, and sorts its own scores into "above d0" (ballots
 //     straight into a bitmap of selected positions) and "in d0" (candidates, compacted in
 //     index order into the chunk's list).
+//  Problems of at most 1024 scores (the heads) are selected whole by one block of the first
+//  launch (rank by counting), and the other two kernels skip them.
 //  3. topk_finish_kernel: one block per row gathers the candidates (typically 1-3 % of n),
 //     resolves the remaining 21 key bits with two more histogram passes, takes the ties at
 //     the threshold key in index order, sets their bits, and turns the bitmap into the
@@ -87,12 +89,41 @@ __device__ __forceinline__ const TopkProb& prob_of(const TopkArgs& a) {
   return blockIdx.z == 0 ? a.p[0] : a.p[1];
 }
 
+// Problems of at most kTkSmall scores (the heads) are selected whole by one block inside the
+// first launch: the rank of score i is the number of scores ahead of it (a larger key, or the
+// same key at a lower index), score i is selected when its rank is below k, and a block scan of
+// the selected flags gives the ascending list. Exact, with the same keys and tie rule.
+constexpr int kTkSmall = kTkBlock;
+__device__ __forceinline__ void topk_small(const TopkProb& P, int b, unsigned* s_key, unsigned* s_scan) {
+  const int n = P.n, k = P.k, tid = threadIdx.x;
+  const float* sc = P.scores + (long long)b * n;
+  const unsigned key = tid < n ? order_key(sc[tid]) : 0u;
+  if (tid < n) s_key[tid] = key;
+  __syncthreads();
+  bool sel = false;
+  if (tid < n) {
+    unsigned r = 0;
+    for (int j = 0; j < n; ++j) {
+      const unsigned kj = s_key[j];
+      r += (kj > key || (kj == key && j < tid)) ? 1u : 0u;
+    }
+    sel = r < (unsigned)k;
+  }
+  unsigned tot;
+  const unsigned pos = block_scan(sel ? 1u : 0u, &tot, s_scan);
+  if (sel) P.out[(long long)b * k + pos] = tid;
+}
+
 // 1. per-chunk histograms of bits 31..21 -> part[b][chunk][2048]
 __global__ __launch_bounds__(kTkBlock) void topk_hist_kernel(TopkArgs a) {
   __shared__ unsigned s_hist[kTkCopies][kTkBins];
   const TopkProb& P = prob_of(a);
   const int c = blockIdx.x, b = blockIdx.y, n = P.n, tid = threadIdx.x;
   const int nch = (n + kTopkChunk - 1) / kTopkChunk;
+  if (n <= kTkSmall) {   // block-uniform: the whole problem in this launch
+    if (c == 0 && P.k > 0) topk_small(P, b, &s_hist[0][0], &s_hist[1][0]);
+    return;
+  }
   if (P.k <= 0 || P.k >= n || c >= nch) return;
   const float* sc = P.scores + (long long)b * n;
   for (int i = tid; i < kTkCopies * kTkBins; i += kTkBlock) (&s_hist[0][0])[i] = 0u;
@@ -128,7 +159,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_classify_kernel(TopkArgs a) {
   const int c = blockIdx.x, b = blockIdx.y, n = P.n, k = P.k, tid = threadIdx.x;
   const int lane = tid % kWave, w = tid / kWave;
   const int nch = (n + kTopkChunk - 1) / kTopkChunk;
-  if (k <= 0 || k >= n || c >= nch) return;
+  if (n <= kTkSmall || k <= 0 || k >= n || c >= nch) return;   // small problems are done
   const float* sc = P.scores + (long long)b * n;
   // every load of the block is issued before the first one is used
   unsigned key[kTkEpt];
@@ -218,7 +249,7 @@ __global__ __launch_bounds__(kTkBlock) void topk_finish_kernel(TopkArgs a) {
   const TopkProb& P = prob_of(a);
   const int b = blockIdx.x, n = P.n, k = P.k, tid = threadIdx.x;
   const int copy = (tid / kWave) % kTkCopies;
-  if (k <= 0) return;
+  if (k <= 0 || n <= kTkSmall) return;   // small problems are done
   int32_t* out = P.out + (long long)b * k;
   if (k >= n) {
     for (int i = tid; i < n; i += kTkBlock) out[i] = i;
@@ -371,6 +402,7 @@ hipError_t launch_topk(const TopkArgs& a, int B, hipStream_t s) {
   const int nch = (nmax + kTopkChunk - 1) / kTopkChunk;
   const dim3 grid(nch, B, a.nprob);
   hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(kTkBlock), 0, s, a);
+  if (nmax <= kTkSmall) return hipGetLastError();   // every problem was selected whole
   hipLaunchKernelGGL(topk_classify_kernel, grid, dim3(kTkBlock), 0, s, a);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(B, 1, a.nprob), dim3(kTkBlock), 0, s, a);
   return hipGetLastError();
