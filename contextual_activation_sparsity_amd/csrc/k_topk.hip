@@ -14,7 +14,7 @@
 //     holding the k-th largest key, and sorts its own scores into "above d0" (ballots
 //     straight into a bitmap of selected positions) and "in d0" (candidates, compacted in
 //     index order into the chunk's list).
-//  Problems of at most 1024 scores (the heads) are selected whole by one block of the first
+//  Problems of at most 256 scores (the heads) are selected whole by one block of the first
 //  launch (rank by counting), and the other two kernels skip them.
 //  3. topk_finish_kernel: one block per row gathers the candidates (typically 1-3 % of n),
 //     resolves the remaining 21 key bits with two more histogram passes, takes the ties at
@@ -93,19 +93,27 @@ __device__ __forceinline__ const TopkProb& prob_of(const TopkArgs& a) {
 // first launch: the rank of score i is the number of scores ahead of it (a larger key, or the
 // same key at a lower index), score i is selected when its rank is below k, and a block scan of
 // the selected flags gives the ascending list. Exact, with the same keys and tie rule.
-constexpr int kTkSmall = kTkBlock;
+constexpr int kTkSmall = 256;
+static_assert(kTkSmall <= kTkBlock, "one score per thread");
 __device__ __forceinline__ void topk_small(const TopkProb& P, int b, unsigned* s_key, unsigned* s_scan) {
   const int n = P.n, k = P.k, tid = threadIdx.x;
   const float* sc = P.scores + (long long)b * n;
   const unsigned key = tid < n ? order_key(sc[tid]) : 0u;
-  if (tid < n) s_key[tid] = key;
+  // keys padded with 0 to a multiple of 4: a pad (index >= n > tid) is never ahead of a score
+  if (tid < ((n + 3) & ~3)) s_key[tid] = key;
   __syncthreads();
   bool sel = false;
   if (tid < n) {
     unsigned r = 0;
-    for (int j = 0; j < n; ++j) {
-      const unsigned kj = s_key[j];
-      r += (kj > key || (kj == key && j < tid)) ? 1u : 0u;
+    const u32x4* k4 = reinterpret_cast<const u32x4*>(s_key);
+#pragma unroll 4
+    for (int j4 = 0; j4 < (n + 3) / 4; ++j4) {
+      const u32x4 v = k4[j4];
+      const int j = 4 * j4;
+      r += (v.x > key || (v.x == key && j < tid)) ? 1u : 0u;
+      r += (v.y > key || (v.y == key && j + 1 < tid)) ? 1u : 0u;
+      r += (v.z > key || (v.z == key && j + 2 < tid)) ? 1u : 0u;
+      r += (v.w > key || (v.w == key && j + 3 < tid)) ? 1u : 0u;
     }
     sel = r < (unsigned)k;
   }
@@ -116,7 +124,7 @@ __device__ __forceinline__ void topk_small(const TopkProb& P, int b, unsigned* s
 
 // 1. per-chunk histograms of bits 31..21 -> part[b][chunk][2048]
 __global__ __launch_bounds__(kTkBlock) void topk_hist_kernel(TopkArgs a) {
-  __shared__ unsigned s_hist[kTkCopies][kTkBins];
+  __shared__ __attribute__((aligned(16))) unsigned s_hist[kTkCopies][kTkBins];
   const TopkProb& P = prob_of(a);
   const int c = blockIdx.x, b = blockIdx.y, n = P.n, tid = threadIdx.x;
   const int nch = (n + kTopkChunk - 1) / kTopkChunk;
