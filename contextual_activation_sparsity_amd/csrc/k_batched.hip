@@ -422,6 +422,9 @@ __global__ void gemm_rows_finish_kernel(GemmRowsArgs a) {
 // ---------------------------------------------------------------------------
 // gemm_cols: down-projection over gathered rows, row groups -> partials
 // ---------------------------------------------------------------------------
+#ifndef DV_COLS_BPC
+#define DV_COLS_BPC 3    // target blocks per CU when choosing the down-projection's row groups
+#endif
 #ifndef DV_COLS_CW
 #define DV_COLS_CW 256   // output columns per block: 512-byte strips of every weight row
 #endif
@@ -630,7 +633,7 @@ hipError_t launch_gemm_rows(const GemmRowsArgs& a_in, int max_rows, int cus, hip
 int gemm_cols_rg(int d, int max_rows, int B, int cus) {
   constexpr int KT = 8 * kGemmBlock / (DV_COLS_CW / 8);
   const int ctiles = (d + DV_COLS_CW - 1) / DV_COLS_CW;
-  int rg = (3 * cus + ctiles - 1) / ctiles;               // about three blocks per CU
+  int rg = (DV_COLS_BPC * cus + ctiles - 1) / ctiles;     // about DV_COLS_BPC blocks per CU
   const int cap = max(1, max_rows / (2 * KT));            // at least 2 tiles of rows per group
   rg = min(rg, cap);
   rg = min(rg, kBatchMaxRG);
