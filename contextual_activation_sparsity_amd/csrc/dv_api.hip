@@ -252,9 +252,9 @@ dv_status run_predict_stage2(const dv_dims* d, const dv_predictor* P, int B, flo
                              const float* z, int cus, hipStream_t st);
 
 // The batched path (union of the rows' selections on the matrix cores) serves fp16 weights
-// and 4..32 rows; other batches run every row through the single-row kernels.
+// and 3..32 rows; other batches run every row through the single-row kernels.
 #ifndef DV_BATCH_MIN
-#define DV_BATCH_MIN 4   // measured crossover at OPT-175B shape: below it, rows run one by one faster
+#define DV_BATCH_MIN 3   // measured crossover at OPT-175B shape: below it, rows run one by one faster
 #endif
 bool batched(const dv_dims* d, int B) { return B >= DV_BATCH_MIN && B <= dv::kBatchMax && is_f16(d); }
 

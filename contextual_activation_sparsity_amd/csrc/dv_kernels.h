@@ -189,6 +189,8 @@ struct GemmRowsArgs {                // out[b][i] = act(W[row_i] . X[b] + bias[r
   const _Float16* X_lo_b;            //   n_rows_a is a multiple of 64, so a block's rows use one input
   float* outf_b;                     // nullable (kGemmOutF32): outputs of W_b's rows, [B][ldo_b]
   long long ldo_b;
+  int dyn_slots;                     // set by the launcher: > 0 when the K split follows the device-side row
+                                     //   count (ks = dyn_slots / tiles, at most ksplit)
 };
 constexpr int kRowsMaxSplit = 32;       // K slices of a short up-projection
 constexpr int kRowsSplitMaxRows = 4096; // only launches of at most this many rows split K

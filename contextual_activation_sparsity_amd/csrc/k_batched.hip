@@ -264,6 +264,12 @@ __global__ __launch_bounds__(kNormBlock) void rows_norm_f16_kernel(const float* 
 // ---------------------------------------------------------------------------
 constexpr int kGemmBlock = 256;   // 4 waves
 
+// K slices of a launch whose split follows the device-side tile count.
+__device__ __forceinline__ int rows_dyn_ks(const GemmRowsArgs& a, int tiles) {
+  const int ks = tiles > 0 ? a.dyn_slots / tiles : 1;
+  return ks < 1 ? 1 : (ks > a.ksplit ? a.ksplit : ks);
+}
+
 // Epilogue of one output (gathered row i, batch row b): bias, ReLU, the row's own mask, and
 // the store in the launch's output mode.
 __device__ __forceinline__ void rows_store(const GemmRowsArgs& a, int i, int b, float acc) {
@@ -310,7 +316,17 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int lr = lane % 16, lg = lane / 16;
   const int nrows = (a.n_groups_sel ? *a.n_groups_sel : a.n_groups) * a.G;
-  const int r0 = blockIdx.x * 64;
+  // (row tile, K slice) of this block: grid.y slices, or with a device-side split the slices
+  // that keep about dyn_slots blocks busy for the union's actual number of tiles.
+  int tile = blockIdx.x, slice = blockIdx.y, ks = gridDim.y;
+  if (a.dyn_slots > 0) {
+    const int tiles = (nrows + 63) / 64;
+    ks = rows_dyn_ks(a, tiles);
+    if ((int)blockIdx.x >= tiles * ks) return;   // block-uniform
+    tile = blockIdx.x / ks;
+    slice = blockIdx.x - tile * ks;
+  }
+  const int r0 = tile * 64;
   if (r0 >= nrows) return;   // block-uniform
   const half_t* W = reinterpret_cast<const half_t*>(a.W);
   // loader: thread -> rows lrow + 8*q (q < 8), 8 halfs at k = kk
@@ -361,8 +377,8 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
   for (int nt = 0; nt < NT; ++nt) acc[nt] = f4v{0.f, 0.f, 0.f, 0.f};
   // K chunks of this block's slice (grid.y slices when K is split over blocks)
   const int nch = (a.d + kRowsKC - 1) / kRowsKC;
-  const int kfirst = (int)((long long)nch * blockIdx.y / gridDim.y) * kRowsKC;
-  const int klast = min(a.d, (int)((long long)nch * (blockIdx.y + 1) / gridDim.y) * kRowsKC);
+  const int kfirst = (int)((long long)nch * slice / ks) * kRowsKC;
+  const int klast = min(a.d, (int)((long long)nch * (slice + 1) / ks) * kRowsKC);
   if (kfirst < klast) load(kfirst);
   for (int k0 = kfirst; k0 < klast; k0 += kRowsKC) {   // block-uniform
     __syncthreads();   // the previous chunk's readers are done
@@ -397,7 +413,7 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
     for (int nt = 0; nt < NT; ++nt) {
       const int b = nt * 16 + lr;
       if (b >= a.B) continue;
-      if (gridDim.y > 1) a.kpart[((long long)blockIdx.y * a.B + b) * a.kld + i] = acc[nt][e];
+      if (ks > 1) a.kpart[((long long)slice * a.B + b) * a.kld + i] = acc[nt][e];
       else rows_store(a, i, b, acc[nt][e]);
     }
   }
@@ -409,19 +425,28 @@ __global__ void gemm_rows_finish_kernel(GemmRowsArgs a) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   const int b = blockIdx.y;
   if (i >= nrows) return;
+  const int ks = a.dyn_slots > 0 ? rows_dyn_ks(a, (nrows + 63) / 64) : a.ksplit;
+  if (ks == 1) return;   // the up-projection stored its outputs itself
   float p[kRowsMaxSplit];   // every slice's partial in flight together, summed in slice order
 #pragma unroll
-  for (int q = 0; q < kRowsMaxSplit; ++q) p[q] = q < a.ksplit ? a.kpart[((long long)q * a.B + b) * a.kld + i] : 0.f;
+  for (int q = 0; q < kRowsMaxSplit; ++q) p[q] = q < ks ? a.kpart[((long long)q * a.B + b) * a.kld + i] : 0.f;
   float v = 0.f;
 #pragma unroll
   for (int q = 0; q < kRowsMaxSplit; ++q)
-    if (q < a.ksplit) v += p[q];
+    if (q < ks) v += p[q];
   rows_store(a, i, b, v);
 }
 
 // ---------------------------------------------------------------------------
 // gemm_cols: down-projection over gathered rows, row groups -> partials
 // ---------------------------------------------------------------------------
+#ifndef DV_ROWS_DYN_MAXB
+#define DV_ROWS_DYN_MAXB 8    // union up-projections of at most this many rows split K on the device
+#endif
+static_assert(DV_ROWS_DYN_MAXB <= 16, "the device-side split launches the 16-row activation tile");
+#ifndef DV_ROWS_DYN_BPC
+#define DV_ROWS_DYN_BPC 3     // blocks per CU the device-side K split aims for
+#endif
 #ifndef DV_COLS_BPC
 #define DV_COLS_BPC 3    // target blocks per CU when choosing the down-projection's row groups
 #endif
@@ -614,8 +639,25 @@ hipError_t launch_gemm_rows(const GemmRowsArgs& a_in, int max_rows, int cus, hip
   const int tiles = (max_rows + 63) / 64;
   const int nch = (a.d + kRowsKC - 1) / kRowsKC;
   int ks = 1;
-  if (a.kpart != nullptr && max_rows <= kRowsSplitMaxRows && tiles < 2 * cus && a.kld >= max_rows)
+  a.dyn_slots = 0;
+  if (a.kpart != nullptr && max_rows <= kRowsSplitMaxRows && tiles < 2 * cus && a.kld >= max_rows) {
     ks = std::max(1, std::min({(2 * cus + tiles - 1) / tiles, nch, kRowsMaxSplit}));
+  } else if (a.kpart != nullptr && a.n_groups_sel != nullptr && !split && a.B <= DV_ROWS_DYN_MAXB) {
+    // A union launch: its row count is known only on the device, so blocks pick their K slice
+    // from it, up to the slices the partial buffer holds at this launch's largest row count.
+    const int cap = (int)std::min<long long>(kRowsMaxSplit, (long long)kRowsMaxSplit * kRowsSplitMaxRows / max_rows);
+    const int kmax = std::min(nch, cap);
+    if (kmax >= 2) {
+      a.ksplit = kmax;
+      a.dyn_slots = DV_ROWS_DYN_BPC * cus;
+      a.kld = max_rows;
+      hipLaunchKernelGGL((gemm_rows_lds_kernel<1, false>), dim3(tiles * kmax, 1), dim3(256), 0, s, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(gemm_rows_finish_kernel, dim3((max_rows + 255) / 256, a.B), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   a.ksplit = ks;
   if (a.B <= 16) {
     if (split) launch_rows_lds<1, true>(a, max_rows, ks, s);

@@ -1,6 +1,6 @@
-"""Batched decode against the fp64 oracle applied row by row (GPU). Batches of 4..32 rows
-with fp16 weights run on the union of the rows' selections (matrix cores); smaller batches
-run row by row; both are covered.
+"""Batched decode against the fp64 oracle applied row by row (GPU). Batches of 3..32 rows
+with fp16 weights run on the union of the rows' selections (matrix cores); 2 rows run row
+by row; both are covered.
 
 Each row's result depends only on its own neuron and head sets; the union only shares the
 weight reads. Rows draw their sets from a Zipf(1.1)-skewed popularity (Gumbel-top-k of
@@ -65,7 +65,7 @@ def run_layer(dv, w, t, x, S, Sh, ws=None):
 
 
 @pytest.mark.parametrize("w", [W_C2, W_RAG16], ids=["opt6.7b-shape", "ragged"])
-@pytest.mark.parametrize("B", [2, 5, 8, 16, 17, 32])
+@pytest.mark.parametrize("B", [2, 3, 5, 8, 16, 17, 32])
 def test_batched_layer_matches_rowwise_oracle(dv, host_layers, w, B):
     t = host_layers[w.name]
     wc = w.with_(batch=B)
