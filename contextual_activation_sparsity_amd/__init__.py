@@ -21,13 +21,14 @@ from typing import Dict, Optional, Sequence, Tuple
 import torch
 
 from . import _lib
-from ._lib import DejavuError  # noqa: F401
+from ._lib import DV_IDX_DUPLICATE, DV_IDX_ORDER, DV_IDX_RANGE, DejavuError  # noqa: F401
 
 __all__ = ["Dims", "LayerWeights", "PredictorWeights", "workspace", "stack_workspace", "dv_predict",
            "dv_topk", "dv_sparse_mlp", "dv_sparse_attn", "dv_layer_step", "dv_lookahead_stack",
            "dv_decode_step", "dv_layer_labels", "dv_predictor_train_workspace_bytes", "dv_predictor_train_step",
            "dv_workspace_bytes", "dv_stack_workspace_bytes", "dv_topk_workspace_bytes", "dv_block_scores",
-           "dv_sparse_mlp_blocked", "require_gpu", "DejavuError"]
+           "dv_sparse_mlp_blocked", "dv_check_indices", "require_gpu", "DejavuError",
+           "DV_IDX_RANGE", "DV_IDX_ORDER", "DV_IDX_DUPLICATE"]
 
 _DT = {"f32": (_lib.DV_F32, torch.float32), "f16": (_lib.DV_F16, torch.float16)}
 
@@ -157,6 +158,17 @@ def dv_block_scores(scores: torch.Tensor, bs: int, out: torch.Tensor, stream=Non
     B, n = scores.shape
     st = _lib.lib().dv_block_scores(_ptr(scores), B, n, bs, _ptr(out), _stream(stream))
     _lib.check("dv_block_scores", st)
+
+
+def dv_check_indices(idx: Optional[torch.Tensor], n: int, status: torch.Tensor, k: Optional[int] = None,
+                     stream=None) -> None:
+    """status[b] (int32 device tensor [B]) = OR of DV_IDX_RANGE / DV_IDX_ORDER / DV_IDX_DUPLICATE
+    for row b of idx [B][k] (int32 device tensor) against the bound n; 0 when the row is valid."""
+    B = status.numel()
+    if k is None:
+        k = 0 if idx is None else idx.shape[-1]
+    st = _lib.lib().dv_check_indices(_ptr(idx), B, k, n, _ptr(status), _stream(stream))
+    _lib.check("dv_check_indices", st)
 
 
 def dv_sparse_mlp_blocked(dims: Dims, layer: LayerWeights, xn: torch.Tensor, blocks: Optional[torch.Tensor], kb: int,

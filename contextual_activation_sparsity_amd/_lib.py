@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdejavu_hip.so")
 
 DV_F32, DV_F16 = 0, 1
+DV_IDX_RANGE, DV_IDX_ORDER, DV_IDX_DUPLICATE = 1, 2, 4
 STATUS = {0: "DV_OK", 1: "DV_ERR_NULL", 2: "DV_ERR_DIMS", 3: "DV_ERR_K", 4: "DV_ERR_DTYPE",
           5: "DV_ERR_ALIGN", 6: "DV_ERR_KV", 7: "DV_ERR_WORKSPACE", 8: "DV_ERR_HIP"}
 
@@ -85,6 +86,7 @@ SIGNATURES = {
     "dv_sparse_mlp_blocked": (c_int32, [ctypes.POINTER(DvDims), ctypes.POINTER(DvLayer), c_void_p, c_int32, c_void_p,
                                         c_int32, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "dv_topk_workspace_bytes": (c_size_t, [c_int32, c_int32]),
+    "dv_check_indices": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "dv_timing_start": (c_int32, [c_int32]),
     "dv_timing_stop": (c_int32, [ctypes.POINTER(ctypes.c_float), c_int32]),
     "dv_status_str": (ctypes.c_char_p, [c_int32]),

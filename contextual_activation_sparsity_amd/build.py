@@ -30,7 +30,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
-SOURCES = ["dv_api.hip", "k_rowdot.hip", "k_rowaxpy.hip", "k_attn.hip", "k_topk.hip", "k_batched.hip", "k_blocked.hip", "k_train.hip"]
+SOURCES = ["dv_api.hip", "k_rowdot.hip", "k_rowaxpy.hip", "k_attn.hip", "k_topk.hip", "k_batched.hip", "k_blocked.hip",
+           "k_train.hip", "k_check.hip"]
 
 
 def _run(cmd):

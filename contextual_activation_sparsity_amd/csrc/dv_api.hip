@@ -4,8 +4,8 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
-#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -27,6 +27,13 @@ dv_status fail(dv_status s, const char* fmt, ...) {
   return s;
 }
 
+}  // namespace
+
+// Records the detail of a failed call for dv_last_error() (other sources of the library).
+dv_status dv::record_error(dv_status s, const char* msg) { return fail(s, "%s", msg); }
+
+namespace {
+
 #define DV_HIP(call)                                                                      \
   do {                                                                                    \
     hipError_t e_ = (call);                                                               \
@@ -46,9 +53,10 @@ struct DeviceInfo {
   int cus = 0;
   hipEvent_t ev_in = nullptr, ev_sel[2] = {nullptr, nullptr};
 };
-std::mutex g_mu;
-std::map<int, int> g_cus;                  // compute units per device
-thread_local std::map<int, DeviceInfo> t_dev;   // the stack's fork/join events: per device and thread
+// Fixed-size tables indexed by device ordinal: looking a device up never allocates.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];                 // compute units per device (0: not queried yet)
+thread_local DeviceInfo t_dev[kMaxDevices];          // the stack's fork/join events: per device and thread
 
 // Compute units of the current device and, with events, this thread's stack events on it.
 // Events are per thread so that stack calls from different host threads never record or
@@ -56,14 +64,15 @@ thread_local std::map<int, DeviceInfo> t_dev;   // the stack's fork/join events:
 dv_status device_info(DeviceInfo** out, bool events) {
   int dev = 0;
   DV_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DV_ERR_HIP, "device ordinal %d beyond %d", dev, kMaxDevices);
   DeviceInfo& di = t_dev[dev];
   if (di.cus == 0) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    int& cus = g_cus[dev];
+    int cus = g_cus[dev].load(std::memory_order_relaxed);
     if (cus == 0) {
       int n = 0;
       DV_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev));
       cus = n > 0 ? n : 1;
+      g_cus[dev].store(cus, std::memory_order_relaxed);
     }
     di.cus = cus;
   }
@@ -694,6 +703,18 @@ dv_status dv_block_scores(const float* scores, int32_t B, int32_t n, int32_t bs,
   if (scores == nullptr || out == nullptr) return fail(DV_ERR_NULL, "scores and out must be given");
   DV_TRY(check_ptr(scores, "scores"));   // read as 16-byte chunks when bs % 4 == 0
   DV_HIP(dv::launch_block_scores(scores, B, n, bs, out, stream));
+  return DV_OK;
+}
+
+dv_status dv_check_indices(const int32_t* idx, int32_t B, int32_t k, int32_t n, int32_t* status, hipStream_t stream) {
+  if (B <= 0 || n <= 0) return fail(DV_ERR_DIMS, "B and n must be positive");
+  if (k < 0 || k > n) return fail(DV_ERR_K, "k=%d outside [0, %d]", k, n);
+  if (status == nullptr) return fail(DV_ERR_NULL, "status is NULL");
+  if (k > 0 && idx == nullptr) return fail(DV_ERR_NULL, "idx is NULL");
+  if (reinterpret_cast<uintptr_t>(status) % alignof(int32_t) != 0 ||
+      reinterpret_cast<uintptr_t>(idx) % alignof(int32_t) != 0)
+    return fail(DV_ERR_ALIGN, "idx and status must be 4-byte aligned");
+  DV_HIP(dv::launch_check_indices(idx, B, k, n, status, stream));
   return DV_OK;
 }
 

@@ -3,7 +3,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "dejavu_hip.h"
+
 namespace dv {
+
+// Host side: sets the thread's dv_last_error() text and returns s.
+dv_status record_error(dv_status s, const char* msg);
 
 // ---------------------------------------------------------------------------
 // Gather row-dot ("GEMV1"): out[b][i] = act(dot(W[row_b(i)], xhat_b) + bias[row_b(i)])
@@ -216,6 +221,12 @@ hipError_t launch_heads_to_union(const float* o, int kh, int dh, const int32_t* 
                                  int hwords, int B, int max_uh, _Float16* C, long long ldc, hipStream_t s);
 // out[b][c] = sum_rg partial[b][rg][c] (group order) + bias[c] + resid[b][c]
 hipError_t launch_axpy_reduce(const RowAxpyArgs& a, int B, hipStream_t s);
+
+// Index-list validation (k_check.hip): status[b] = OR of the flags row b's list breaks.
+constexpr int kIdxRange = 1;       // an entry outside [0, n)
+constexpr int kIdxOrder = 2;       // an entry smaller than its predecessor
+constexpr int kIdxDuplicate = 4;   // an entry equal to its predecessor
+hipError_t launch_check_indices(const int32_t* idx, int B, int k, int n, int32_t* status, hipStream_t s);
 
 // Blocked-channel scores (k_blocked.hip): out[b][j] = max of scores[b][j*bs .. j*bs+bs-1].
 hipError_t launch_block_scores(const float* scores, int B, int n, int bs, float* out, hipStream_t s);

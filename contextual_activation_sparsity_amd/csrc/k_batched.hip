@@ -391,14 +391,14 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
     __syncthreads();
     if (k0 + kRowsKC < klast) load(k0 + kRowsKC);
     const int nks = min(kRowsKC, a.d - k0 + 31) / 32;   // k-steps holding data (the rest are zero)
-    for (int ks = 0; ks < nks; ++ks) {
-      const h8v af = *reinterpret_cast<const h8v*>(&s_w[(16 * wv + lr) * kRowsLdk + 32 * ks + 8 * lg]);
+    for (int kstep = 0; kstep < nks; ++kstep) {
+      const h8v af = *reinterpret_cast<const h8v*>(&s_w[(16 * wv + lr) * kRowsLdk + 32 * kstep + 8 * lg]);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const h8v bf = *reinterpret_cast<const h8v*>(&s_x[0][(16 * nt + lr) * kRowsLdk + 32 * ks + 8 * lg]);
+        const h8v bf = *reinterpret_cast<const h8v*>(&s_x[0][(16 * nt + lr) * kRowsLdk + 32 * kstep + 8 * lg]);
         acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[nt], 0, 0, 0);
         if constexpr (SPLIT) {
-          const h8v bl = *reinterpret_cast<const h8v*>(&s_x[XL - 1][(16 * nt + lr) * kRowsLdk + 32 * ks + 8 * lg]);
+          const h8v bl = *reinterpret_cast<const h8v*>(&s_x[XL - 1][(16 * nt + lr) * kRowsLdk + 32 * kstep + 8 * lg]);
           acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bl, acc[nt], 0, 0, 0);
         }
       }
@@ -551,14 +551,14 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
     if (cb < MT * 16) *reinterpret_cast<h8v*>(&s_c[cb * LDK + ck]) = ccur;
     __syncthreads();
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int kstep = 0; kstep < KS; ++kstep)
 #pragma unroll
       for (int i = 0; i < CTW; ++i) {
         const int cl = (wv * CTW + i) * 16 + lr;
-        const h8v bf = *reinterpret_cast<const h8v*>(&s_w[cl * LDK + 32 * ks + 8 * lg]);
+        const h8v bf = *reinterpret_cast<const h8v*>(&s_w[cl * LDK + 32 * kstep + 8 * lg]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          const h8v af = *reinterpret_cast<const h8v*>(&s_c[(16 * mt + lr) * LDK + 32 * ks + 8 * lg]);
+          const h8v af = *reinterpret_cast<const h8v*>(&s_c[(16 * mt + lr) * LDK + 32 * kstep + 8 * lg]);
           acc[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[i][mt], 0, 0, 0);
         }
       }

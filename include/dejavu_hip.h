@@ -31,7 +31,8 @@
  *   - Weights are stored NEURON-MAJOR so every selected row is one contiguous burst:
  *     w1t[j] is column j of W1, w2[j] is row j of W2, p2_mlp[j] scores neuron j.
  *   - Index lists are int32, ascending, unique and in range (dv_topk produces exactly
- *     that). An out-of-range entry contributes nothing (it is never dereferenced).
+ *     that; dv_check_indices checks lists from elsewhere). An out-of-range entry
+ *     contributes nothing (it is never dereferenced).
  *   - Row length d_model and both predictor ranks must be multiples of 8 (fp16) or 4
  *     (fp32), every pointer 16-byte aligned (DV_ERR_ALIGN otherwise).
  */
@@ -115,6 +116,26 @@ dv_status dv_sparse_mlp(const dv_dims* dims, const dv_layer* layer, const float*
  *   NaNs scores -inf). 1 <= bs <= 4096 and n % bs == 0; scores 16-byte aligned. Rank blocks
  *   with dv_topk. */
 dv_status dv_block_scores(const float* scores, int32_t B, int32_t n, int32_t bs, float* out, hipStream_t stream);
+
+/* Opt-in validation of index lists a caller supplies instead of taking them from dv_topk.
+ * Every call that gathers by index (dv_sparse_mlp, dv_sparse_attn, dv_layer_step, the
+ * blocked MLP) expects each row's list ascending, without repeats and inside [0, n): the
+ * form the predictor hands the sparse forward in DejaVu Guide, "Step-by-Step
+ * Implementation" (sorted indices). A list that breaks it gives path-dependent results (a
+ * repeated neuron counts twice on the row-wise path and once on the batched union path).
+ *   idx [B][k] int32 (device), n the exclusive bound (d_ffn, n_heads or the block count);
+ *   status [B] int32 (device) receives, per row, the OR of:
+ *     DV_IDX_RANGE     an entry < 0 or >= n,
+ *     DV_IDX_ORDER     an entry smaller than the one before it,
+ *     DV_IDX_DUPLICATE an entry equal to the one before it;
+ *   0 means the row's list is valid. In an ascending list every repeat is adjacent, so a
+ *   row with DV_IDX_ORDER clear has DV_IDX_DUPLICATE set exactly when it repeats an entry;
+ *   with DV_IDX_ORDER set, repeats that are not adjacent go unreported.
+ *   B >= 1, n >= 1, 0 <= k <= n (idx may be NULL when k == 0); idx and status 4-byte
+ *   aligned. Asynchronous on `stream`; nothing is read back to the host. */
+enum { DV_IDX_RANGE = 1, DV_IDX_ORDER = 2, DV_IDX_DUPLICATE = 4 };
+dv_status dv_check_indices(const int32_t* idx, int32_t B, int32_t k, int32_t n, int32_t* status,
+                           hipStream_t stream);
 
 /* Sparse ReLU MLP over whole blocks of bs consecutive neurons (same section).
  *   blocks [B][kb]: ascending block ids (block j is neurons j*bs .. j*bs+bs-1); the result

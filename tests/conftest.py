@@ -19,3 +19,21 @@ def dv():
     import contextual_activation_sparsity_amd as pkg
     pkg.require_gpu()
     return pkg
+
+
+def pytest_terminal_summary(terminalreporter):
+    """How many chained set comparisons differed from the oracle's own top-k, and by how much
+    (printed when any GPU test compared sets)."""
+    try:
+        from helpers import SET_DRIFT
+    except ImportError:
+        return
+    if not SET_DRIFT:
+        return
+    rows = len(SET_DRIFT)
+    differ = [r for r in SET_DRIFT if r[3] > 0]
+    worst = max(SET_DRIFT, key=lambda r: r[3])
+    terminalreporter.write_line(
+        f"selected-set drift: {rows} rows compared with the oracle's own top-k, {len(differ)} differ at near ties; "
+        f"largest difference {worst[3]} indices ({worst[0]}, row {worst[1]}, k {worst[2]}, "
+        f"{worst[4]} oracle scores inside the tie band)")

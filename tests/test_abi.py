@@ -196,3 +196,16 @@ def test_validation_codes_training():
     assert h(ctypes.byref(d), ctypes.byref(L), FAKE, 0, FAKE, FAKE, 0, FAKE, None, None, FAKE, 1 << 30, None) == 2
     assert h(ctypes.byref(d), ctypes.byref(L), FAKE, 2, FAKE, FAKE, 129, FAKE, None, None, FAKE, 1 << 30, None) == 6
     assert h(ctypes.byref(d), ctypes.byref(L), FAKE, 2, FAKE, FAKE, 0, FAKE, None, None, FAKE, 64, None) == 7
+
+
+def test_validation_codes_check_indices():
+    f = _lib.lib().dv_check_indices
+    assert f(FAKE, 0, 4, 10, FAKE, None) == 2        # B <= 0: DV_ERR_DIMS
+    assert f(FAKE, 1, 4, 0, FAKE, None) == 2         # n <= 0
+    assert f(FAKE, 1, 11, 10, FAKE, None) == 3       # k > n: DV_ERR_K
+    assert f(FAKE, 1, -1, 10, FAKE, None) == 3
+    assert f(FAKE, 1, 4, 10, None, None) == 1        # status NULL: DV_ERR_NULL
+    assert f(None, 1, 4, 10, FAKE, None) == 1        # idx NULL with k > 0
+    assert f(FAKE + 2, 1, 4, 10, FAKE, None) == 5    # misaligned idx: DV_ERR_ALIGN
+    assert f(FAKE, 1, 4, 10, FAKE + 1, None) == 5    # misaligned status
+    assert b"status" in _lib.lib().dv_last_error()

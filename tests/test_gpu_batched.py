@@ -146,10 +146,12 @@ def test_batched_edge_cases(dv, host_layers, case):
         close(got - ref["h1"], ref["y_m"], f"{case} y_m")
 
 
-def test_batched_deterministic(dv, host_layers):
+@pytest.mark.parametrize("B", [8, 17])
+def test_batched_deterministic(dv, host_layers, B):
+    """Two runs give the same bits: at B = 8 the up-projections split K on the device (the
+    slice count follows the union's device-side size), at B = 17 they do not."""
     w = W_C2
     t = host_layers[w.name]
-    B = 17
     x = synth.x_input(w.with_(batch=B), step=8)
     S = zipf_sets(w, B, w.d_ffn, w.k, "sel_mlp")
     Sh = zipf_sets(w, B, w.n_heads, w.kh, "sel_head")
@@ -219,14 +221,16 @@ def test_batched_stack_two_streams_equal_serial(dv):
 
 
 @pytest.mark.timeout(900)
-def test_opt175b_batched_full_size_sampled_rows(dv):
-    """The OPT-175B-shaped layer at B = 32 (KV 1024, Zipf selections) on the union path, in
-    the launch configuration the batched bench times; three sampled rows checked against the
-    oracle on their regenerated selected rows (output, MLP part and the appended k/v), and
-    the batched predictor's scores of those rows against the oracle's."""
+@pytest.mark.parametrize("B", [8, 32])
+def test_opt175b_batched_full_size_sampled_rows(dv, B):
+    """The OPT-175B-shaped layer at B = 8 (up-projections split K on the device) and B = 32
+    (KV 1024, Zipf selections) on the union path, in the launch configuration the batched
+    bench times; three sampled rows checked against the oracle on their regenerated selected
+    rows (output, MLP part and the appended k/v), and the batched predictor's scores of those
+    rows against the oracle's."""
     import synth.device as sdev
     from helpers import oracle_layer_compact, predictor_host
-    w = synth.OPT175B_BATCHED.with_(batch=32)
+    w = synth.OPT175B_BATCHED.with_(batch=B)
     B = w.batch
     dims = dims_of(w)
     t = sdev.layer_on_device(w, 0)
@@ -246,7 +250,7 @@ def test_opt175b_batched_full_size_sampled_rows(dv):
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     gm, gh = s_m.cpu().numpy(), s_h.cpu().numpy()
-    rows = (0, 13, 31)
+    rows = (0, B // 2 - 3, B - 1)
     p = predictor_host(w, 0)
     rm, rh = oracle.predict(p["p1_mlp"], p["p2_mlp"], p["p1_head"], p["p2_head"], x[list(rows)])
     assert_scores_close(gm[list(rows)], rm, "full-size s_mlp")
