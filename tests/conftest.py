@@ -25,9 +25,18 @@ def pytest_terminal_summary(terminalreporter):
     """How many chained set comparisons differed from the oracle's own top-k, and by how much
     (printed when any GPU test compared sets)."""
     try:
-        from helpers import SET_DRIFT
+        from helpers import ERRORS, SET_DRIFT
     except ImportError:
         return
+    if ERRORS:
+        by_bar = {}
+        for what, ratio, bar in ERRORS:
+            if ratio > by_bar.get(bar, ("", -1.0))[1]:
+                by_bar[bar] = (what, ratio)
+        for bar in sorted(by_bar):
+            what, ratio = by_bar[bar]
+            terminalreporter.write_line(f"largest layer error held to the internal bar {bar:g} x RMS: "
+                                        f"{ratio:.2e} x RMS ({what})")
     if not SET_DRIFT:
         return
     rows = len(SET_DRIFT)

@@ -59,6 +59,11 @@ def rms(a) -> float:
     return float(np.sqrt(np.mean(a * a))) if a.size else 0.0
 
 
+# Every layer-output comparison, for the end-of-run summary (conftest.py): (what, max-abs
+# error / RMS(ref), internal bar it was held to).
+ERRORS: list = []
+
+
 def assert_close(got, ref, dtype: str, what: str, batch: int = 1, depth: int = 1):
     """Layer bar and the internal bar; `depth` layers of a chain where the oracle runs on its
     own outputs add up to `depth` single-layer errors (the residual stream carries them)."""
@@ -71,6 +76,7 @@ def assert_close(got, ref, dtype: str, what: str, batch: int = 1, depth: int = 1
     if dtype == "f16" and batch >= 2:
         bar = BATCHED_BAR
     bar *= depth
+    ERRORS.append((what, err / scale, bar))
     assert err <= LAYER_TOL * scale, f"{what}: max-abs {err:.3e} > {LAYER_TOL} * RMS {scale:.3e}"
     assert err <= bar * scale, f"{what}: max-abs {err:.3e} > internal bar {bar} * RMS {scale:.3e}"
     return err / scale

@@ -43,7 +43,7 @@ def test_crafted_rows(dv):
         [49, 48, 47, 46],    # descending
     ]
     got = run(dv, rows, n)
-    expect = [0, dv.DV_IDX_DUPLICATE, dv.DV_IDX_ORDER, dv.DV_IDX_RANGE, dv.DV_IDX_RANGE | dv.DV_IDX_ORDER,
+    expect = [0, dv.DV_IDX_DUPLICATE, dv.DV_IDX_ORDER, dv.DV_IDX_RANGE, dv.DV_IDX_RANGE,
               dv.DV_IDX_RANGE | dv.DV_IDX_ORDER | dv.DV_IDX_DUPLICATE, dv.DV_IDX_ORDER]
     assert got.tolist() == expect
     assert np.array_equal(got, host_flags(rows, n))
