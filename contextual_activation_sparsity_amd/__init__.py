@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import DV_IDX_DUPLICATE, DV_IDX_ORDER, DV_IDX_RANGE, DejavuError  # noqa: F401
 
 __all__ = ["Dims", "LayerWeights", "PredictorWeights", "workspace", "stack_workspace", "dv_predict",
-           "dv_topk", "dv_sparse_mlp", "dv_sparse_attn", "dv_layer_step", "dv_lookahead_stack",
+           "dv_topk", "dv_sparse_mlp", "dv_sparse_attn", "dv_layer_step", "dv_layer_step_noalloc", "dv_lookahead_stack",
            "dv_decode_step", "dv_layer_labels", "dv_predictor_train_workspace_bytes", "dv_predictor_train_step",
            "dv_workspace_bytes", "dv_stack_workspace_bytes", "dv_topk_workspace_bytes", "dv_block_scores",
            "dv_sparse_mlp_blocked", "dv_check_indices", "require_gpu", "DejavuError",
@@ -252,6 +252,21 @@ def dv_layer_step(dims: Dims, layer: LayerWeights, pred: Optional[PredictorWeigh
                                   _ptr(k_cache), _ptr(v_cache), t_past, _ptr(x_out), _ptr(idx_out),
                                   _ptr(heads_out), wp, wn, _stream(stream))
     _lib.check("dv_layer_step", st)
+
+
+def dv_layer_step_noalloc(dims: Dims, layer: LayerWeights, pred: Optional[PredictorWeights], x: torch.Tensor,
+                          x_pred: Optional[torch.Tensor], k: int, kh: int, idx_in: Optional[torch.Tensor],
+                          heads_in: Optional[torch.Tensor], k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          t_past: int, x_out: torch.Tensor, idx_out: Optional[torch.Tensor] = None,
+                          heads_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """dv_layer_step without a workspace: the library's fixed per-GPU scratch array serves as one."""
+    d, L = dims.c(), layer.c()
+    p = pred.c() if pred is not None else None
+    st = _lib.lib().dv_layer_step_noalloc(ctypes.byref(d), ctypes.byref(L), ctypes.byref(p) if p is not None else None,
+                                          _ptr(x), _ptr(x_pred), x.shape[0], k, kh, _ptr(idx_in), _ptr(heads_in),
+                                          _ptr(k_cache), _ptr(v_cache), t_past, _ptr(x_out), _ptr(idx_out),
+                                          _ptr(heads_out), _stream(stream))
+    _lib.check("dv_layer_step_noalloc", st)
 
 
 def dv_lookahead_stack(dims: Dims, layers: Sequence[LayerWeights], preds: Sequence[PredictorWeights],

@@ -65,6 +65,9 @@ SIGNATURES = {
                                 c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                 c_void_p]),
+    "dv_layer_step_noalloc": (c_int32, [ctypes.POINTER(DvDims), ctypes.POINTER(DvLayer), ctypes.POINTER(DvPredictor),
+                                        c_void_p, c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dv_lookahead_stack": (c_int32, [ctypes.POINTER(DvDims), ctypes.POINTER(DvLayer),
                                      ctypes.POINTER(DvPredictor), c_int32, c_void_p, c_int32, c_int32,
                                      c_int32, ctypes.POINTER(c_void_p), ctypes.POINTER(c_void_p), c_int32,

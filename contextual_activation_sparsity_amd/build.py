@@ -31,7 +31,7 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 SOURCES = ["dv_api.hip", "k_rowdot.hip", "k_rowaxpy.hip", "k_attn.hip", "k_topk.hip", "k_batched.hip", "k_blocked.hip",
-           "k_train.hip", "k_check.hip"]
+           "k_train.hip", "k_check.hip", "dv_noalloc.hip"]
 
 
 def _run(cmd):

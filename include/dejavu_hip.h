@@ -167,6 +167,24 @@ dv_status dv_layer_step(const dv_dims* dims, const dv_layer* layer, const dv_pre
                         void* v_cache, int32_t t_past, float* x_out, int32_t* idx_out,
                         int32_t* heads_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* dv_layer_step for callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): the same arguments without the
+ * workspace, whose role a fixed device array of the library takes, DV_NOALLOC_SCRATCH_BYTES
+ * long. Each GPU holds its own copy of that array from the first use of the library there
+ * until the process ends; the call allocates nothing.
+ *   - Shapes whose dv_workspace_bytes(dims, B, k, kh) exceeds DV_NOALLOC_SCRATCH_BYTES are
+ *     refused with DV_ERR_WORKSPACE before anything is launched (32 MiB holds every batch up
+ *     to 8 rows at the OPT-175B layer shape, k 2458, kh 19, and any one-row layer up to it).
+ *   - All calls on one GPU share its copy of the array: calls that overlap on one GPU (other
+ *     streams, other host threads) race on it and must be ordered by the caller.
+ *   - Results are bitwise those of dv_layer_step with the same arguments. */
+#define DV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+dv_status dv_layer_step_noalloc(const dv_dims* dims, const dv_layer* layer, const dv_predictor* pred,
+                                const float* x, const float* x_pred, int32_t B, int32_t k, int32_t kh,
+                                const int32_t* idx_in, const int32_t* heads_in, void* k_cache,
+                                void* v_cache, int32_t t_past, float* x_out, int32_t* idx_out,
+                                int32_t* heads_out, hipStream_t stream);
+
 /* A stack of n_layers sparse layers with lookahead prediction ("Asynchronous Lookahead
  * Predictors", "Pipelined Overlap Execution"). The sets of layer l+1 are predicted from
  * the input of layer l on `side_stream` while layer l runs on `stream`; layer 0's sets are

@@ -209,3 +209,20 @@ def test_validation_codes_check_indices():
     assert f(FAKE + 2, 1, 4, 10, FAKE, None) == 5    # misaligned idx: DV_ERR_ALIGN
     assert f(FAKE, 1, 4, 10, FAKE + 1, None) == 5    # misaligned status
     assert b"status" in _lib.lib().dv_last_error()
+
+
+def test_noalloc_refuses_oversized_scratch_before_any_launch():
+    """The allocation-free step refuses shapes whose workspace exceeds its fixed array, with
+    DV_ERR_WORKSPACE, before any HIP call (so this runs without a GPU)."""
+    d = dims(d_model=12288, d_ffn=49152, n_heads=96, head_dim=128, rank_mlp=1000, rank_head=1000, t_max=1025,
+             dtype="f16")
+    assert dv.dv_workspace_bytes(d, 32, 2458, 19) > 32 << 20
+    dd, L = d.c(), layer_struct()
+    P = _lib.DvPredictor(FAKE, FAKE, FAKE, FAKE)
+    st = _lib.lib().dv_layer_step_noalloc(ctypes.byref(dd), ctypes.byref(L), ctypes.byref(P), FAKE, FAKE, 32, 2458, 19,
+                                          None, None, FAKE, FAKE, 100, FAKE, None, None, None)
+    assert st == 7
+    assert b"DV_NOALLOC_SCRATCH_BYTES" in _lib.lib().dv_last_error()
+    st = _lib.lib().dv_layer_step_noalloc(ctypes.byref(dd), ctypes.byref(L), ctypes.byref(P), FAKE, FAKE, 0, 2458, 19,
+                                          None, None, FAKE, FAKE, 100, FAKE, None, None, None)
+    assert st == 2   # invalid arguments: dv_layer_step's own check (B <= 0)
