@@ -78,8 +78,18 @@ def main() -> int:
                     help="batch sizes of --workload batched (comma-separated, each 1..32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference for HBM byte counters)")
-    ap.add_argument("--workload", choices=["stack", "batched", "sweep", "blocked", "decode", "train"], default="stack",
-                    help="stack: the 24-layer OPT-175B-shaped decode step (default); batched: one "
+    ap.add_argument("--shape", choices=["opt6.7b", "opt125m"], default="opt6.7b",
+                    help="layer shape of --workload layer")
+    ap.add_argument("--layer-steps", type=int, default=1000, help="timed steps of --workload layer")
+    ap.add_argument("--sweep-cells", default="",
+                    help="cells of --workload sweep as mlp:head densities, comma-separated (default: all 24)")
+    ap.add_argument("--sweep-layers", type=int, default=8,
+                    help="layers of the lookahead stack that --workload sweep times beside the serial step")
+    ap.add_argument("--workload", choices=["stack", "layer", "batched", "sweep", "blocked", "decode", "train"],
+                    default="stack",
+                    help="stack: the 24-layer OPT-175B-shaped decode step (default); layer: one "
+                         "OPT-6.7B-shaped (or, with --shape opt125m, OPT-125m-shaped) layer, 1000 flushed steps "
+                         "with fresh x; batched: one "
                          "OPT-175B-shaped layer at batch 1..32 with Zipf-skewed selections; sweep: the "
                          "OPT-66B-shaped layer over MLP x head densities; blocked: per-neuron vs "
                          "32/64-neuron block selection of the OPT-175B-shaped MLP; decode: consecutive "
@@ -101,7 +111,7 @@ def main() -> int:
 
     dv.require_gpu()
     if args.workload != "stack":
-        out = {"batched": run_batched, "sweep": run_sweep, "blocked": run_blocked,
+        out = {"layer": run_layer, "batched": run_batched, "sweep": run_sweep, "blocked": run_blocked,
                "decode": run_decode, "train": run_train}[args.workload](args, log)
         print(json.dumps(out), flush=True)
         return 0
@@ -307,64 +317,81 @@ def dense_baselines(dv, w, dims, layers, kcs, vcs, xs, n_steps, log):
     res["library_all_selected"] = {"us_per_layer_token": round(us, 2)}
     log(f"[bench] dense through the library: {us:.1f} us/layer-token")
 
-    H, dh, d, T = w.n_heads, w.head_dim, w.d_model, w.t_past
-
-    def torch_layer(x, lw, kc, vc):
-        xn = (x * torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + 1e-5) * lw.g1).half()
-        qkv = Fn.linear(xn, lw.wqkv.view(H * 3 * dh, d)).float().view(H, 3, dh) + lw.bqkv
-        q = (qkv[:, 0] / dh ** 0.5).half().unsqueeze(-1).contiguous()        # [H][dh][1]
-        K = kc[0, :, :T].contiguous()                                          # [H][T][dh]
-        V = vc[0, :, :T].contiguous()
-        s_past = torch.bmm(K, q).squeeze(-1).float()                           # [H][T]
-        s_cur = (qkv[:, 0] * qkv[:, 1]).sum(-1, keepdim=True) / dh ** 0.5
-        p = torch.softmax(torch.cat([s_past, s_cur], -1), -1)
-        o = torch.bmm(p[:, None, :T].half().contiguous(), V).squeeze(1).float() + p[:, T:] * qkv[:, 2]
-        return o
-
-    # Wo and W2 are stored with one row per input element; torch's dense form needs their
-    # transposes, made once here (outside the timed loop).
-    wo_t = [lw.wo.view(H * dh, d).t().contiguous() for lw in layers[:1]]
-    w2_t = [lw.w2.t().contiguous() for lw in layers[:1]]
-
-    def torch_full(x, l, lw, kc, vc):
-        o = torch_layer(x, lw, kc, vc)
-        h1 = x + Fn.linear(o.reshape(1, H * dh).half(), wo_t[0]).float() + lw.bo
-        xn2 = (h1 * torch.rsqrt(h1.pow(2).mean(-1, keepdim=True) + 1e-5) * lw.g2).half()
-        u = torch.relu(Fn.linear(xn2, lw.w1t).float() + lw.b1)
-        return h1 + Fn.linear(u.half(), w2_t[0]).float() + lw.b2
-
     # torch baseline on layer 0 repeated (its transposed copies exist once); at 3.7 GB per
     # layer nothing stays in cache between repeats.
+    torch_full = torch_dense_layer(w, layers[0], kcs[0], vcs[0], 1)
     reps = max(4, n_steps * 2)
     x = xs[0].clone()
-    torch_full(x, 0, layers[0], kcs[0], vcs[0])
+    torch_full(x)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(reps):
-        torch_full(x, 0, layers[0], kcs[0], vcs[0])
+        torch_full(x)
     e1.record()
     torch.cuda.synchronize()
     us_t = e0.elapsed_time(e1) * 1e3 / reps
     res["torch_dense_layer"] = {"us_per_layer_token": round(us_t, 2),
                                 "note": "F.linear (hipBLASLt) projections + bmm attention, fp16 storage"}
     log(f"[bench] dense torch layer: {us_t:.1f} us/layer-token")
-    del wo_t, w2_t
+    del torch_full
     return res
 
 
-def timed_single_layer(step, n_steps, log):
-    """Median and quartiles of one step's time (HIP events on the current stream), with an
-    untimed 1 GiB write between steps so no weight stays in the 256 MB Infinity Cache."""
+def torch_dense_layer(w, lw, kc, vc, B):
+    """The dense layer in torch for B rows, as a timing comparator: RMSNorm, F.linear
+    (hipBLASLt) projections on the storage type with fp32 results, decode attention by bmm over
+    each row's T past slots and the current token (written to slot T first, as the sparse step
+    appends it; the caches hold t_max = T + 1 slots), ReLU MLP. The transposed copies torch's
+    dense form needs for Wo and W2 are made here, once, outside any timed region."""
+    import torch
+    import torch.nn.functional as Fn
+    H, dh, d, T = w.n_heads, w.head_dim, w.d_model, w.t_past
+    t_max = kc.shape[2]
+    assert t_max == T + 1, "the torch comparator attends over every cache slot"
+    st = lw.wqkv.dtype
+    wqkv = lw.wqkv.view(H * 3 * dh, d)
+    wo_t = lw.wo.view(H * dh, d).t().contiguous()
+    w2_t = lw.w2.t().contiguous()
+    K = kc[:B].view(B * H, t_max, dh)
+    V = vc[:B].view(B * H, t_max, dh)
+    scale = 1.0 / dh ** 0.5
+
+    def f(x):
+        xn = (x * torch.rsqrt(x.pow(2).mean(-1, keepdim=True) + 1e-5) * lw.g1).to(st)
+        qkv = Fn.linear(xn, wqkv).float().view(B, H, 3, dh) + lw.bqkv
+        K[:, T] = qkv[:, :, 1].reshape(B * H, dh).to(st)
+        V[:, T] = qkv[:, :, 2].reshape(B * H, dh).to(st)
+        q = (qkv[:, :, 0] * scale).reshape(B * H, dh, 1).to(st)
+        p = torch.softmax(torch.bmm(K, q).float(), dim=1)                       # [B*H][t_max][1]
+        o = torch.bmm(p.transpose(1, 2).to(st).contiguous(), V).float()          # [B*H][1][dh]
+        h1 = x + Fn.linear(o.reshape(B, H * dh).to(st), wo_t).float() + lw.bo
+        xn2 = (h1 * torch.rsqrt(h1.pow(2).mean(-1, keepdim=True) + 1e-5) * lw.g2).to(st)
+        u = torch.relu(Fn.linear(xn2, lw.w1t).float() + lw.b1)
+        return h1 + Fn.linear(u.to(st), w2_t).float() + lw.b2
+
+    return f
+
+
+def timed_single_layer(step, n_steps, log, work=None):
+    """Median and 10th/90th percentiles of one step's time (HIP events on the current
+    stream), with an untimed 1 GiB write between steps so no weight stays in the 256 MB
+    Infinity Cache. `step(i)` records the device work while a graph is being captured and
+    otherwise only rotates the inputs; the timed work is then one replay of that graph.
+    With `work` given, the timed work is instead the eager call work() (no graph)."""
     import numpy as np
     import torch
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    graph = torch.cuda.CUDAGraph()
-    step(0)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
+    if work is None:
+        graph = torch.cuda.CUDAGraph()
         step(0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step(0)
+        run = graph.replay
+    else:
+        run = work
     for _ in range(2):
-        graph.replay()
+        run()
     torch.cuda.synchronize()
     ts = []
     for i in range(n_steps):
@@ -372,13 +399,175 @@ def timed_single_layer(step, n_steps, log):
         flush.fill_(i & 0xFF)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        graph.replay()
+        run()
         e1.record()
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1) * 1e3)
     del flush
     ts = np.array(ts)
     return float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
+
+
+def run_layer(args, log):
+    """One decoder layer at batch 1 with the sets predicted inline (predictor, top-k, sparse
+    layer), a fresh x for every step: the OPT-6.7B-shaped layer (d 4096, FFN 16384, 32 x 128
+    heads, KV 2048, rank 512, 5 % of the neurons = 820, 7 heads, fp16) or, with --shape
+    opt125m, the OPT-125m-shaped fp32 layer (d 768, FFN 3072, 12 x 64, KV 128, rank 128, 307
+    neurons, 3 heads). Per-step HIP events around graph replays with a 1 GiB write between
+    steps (nothing stays in the 256 MB Infinity Cache); the warm number replays back to back
+    without the write. Beside it: the dense layer through the same library and through torch,
+    and the fp64 oracle on the host on all cores and on one core."""
+    import numpy as np
+    import torch
+    import contextual_activation_sparsity_amd as dv
+    from contextual_activation_sparsity_amd import traffic
+    import synth
+    import synth.device as sdev
+    w = {"opt6.7b": synth.OPT6P7B_LAYER, "opt125m": synth.OPT125M_LAYER}[args.shape]
+    wb = 2 if w.dtype == "f16" else 4
+    dims = dv.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, w.t_max, w.dtype)
+    t = sdev.layer_on_device(w, 0)
+    lw = dv.LayerWeights(**{k: t[k] for k in ("g1", "g2", "wqkv", "bqkv", "wo", "bo", "w1t", "b1", "w2", "b2")})
+    pw = dv.PredictorWeights(**{k: t[k] for k in ("p1_mlp", "p2_mlp", "p1_head", "p2_head")})
+    kc = sdev.kv_on_device(w, "k_cache", 0)
+    vc = sdev.kv_on_device(w, "v_cache", 0)
+    steps = args.layer_steps
+    xs = torch.empty(steps, 1, w.d_model, device="cuda")
+    for i in range(steps):
+        sdev.fill_(xs[i], w.key("x", 0, i), w.x_sigma)
+    x = torch.empty(1, w.d_model, device="cuda")
+    y = torch.empty_like(x)
+    ws = dv.workspace(dims, 1, w.k, w.kh)
+
+    def step(i):
+        if torch.cuda.is_current_stream_capturing():
+            dv.dv_layer_step(dims, lw, pw, x, x, w.k, w.kh, None, None, kc, vc, w.t_past, y, ws=ws)
+        else:
+            x.copy_(xs[i % steps])
+
+    med, p10, p90 = timed_single_layer(step, steps, log)
+    warm = timed_warm(step, steps)
+    tb = traffic.step_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.t_past, w.k, w.kh, wb)
+    gbps = tb["total"] / (med * 1e-6) / 1e9
+    log(f"[bench] layer {w.name}: median {med:.2f} us (p10 {p10:.2f}, p90 {p90:.2f}), warm {warm:.2f} us, "
+        f"{gbps:.0f} GB/s")
+    # dense comparators, flushed like the sparse step
+    idx = torch.arange(w.d_ffn, dtype=torch.int32, device="cuda")[None].contiguous()
+    heads = torch.arange(w.n_heads, dtype=torch.int32, device="cuda")[None].contiguous()
+    wsd = dv.workspace(dims, 1, w.d_ffn, w.n_heads)
+
+    def dstep(i):
+        if torch.cuda.is_current_stream_capturing():
+            dv.dv_layer_step(dims, lw, None, x, None, w.d_ffn, w.n_heads, idx, heads, kc, vc, w.t_past, y, ws=wsd)
+        else:
+            x.copy_(xs[i % steps])
+
+    n_dense = max(20, steps // 10)
+    dmed, _, _ = timed_single_layer(dstep, n_dense, log)
+    tfn = torch_dense_layer(w, lw, kc, vc, 1)
+
+    def tstep(i):
+        if torch.cuda.is_current_stream_capturing():
+            y.copy_(tfn(x))
+        else:
+            x.copy_(xs[i % steps])
+
+    # hipBLASLt refuses stream capture on this image, so torch's layer is timed eagerly
+    tmed, _, _ = timed_single_layer(tstep, n_dense, log, work=lambda: y.copy_(tfn(x)))
+    tmode = "eager"
+    dbytes = traffic.dense_layer_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.t_past, wb)
+    out = {"metric": f"us per sparse decode layer-token (predictor + top-k + layer), {w.name} shape",
+           "value": round(med, 3), "unit": "us/layer-token", "n_gpus": 1, "steps": steps, "higher_is_better": False,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{w.name}: d {w.d_model}, FFN {w.d_ffn}, {w.n_heads} x {w.head_dim} heads, "
+                                  f"KV {w.t_past}, rank {w.rank}, k {w.k}, kh {w.kh}, batch 1, inline prediction, "
+                                  "fresh x per step",
+                      "storage": f"{w.dtype} weights and KV, fp32 activations and accumulation",
+                      "timing": "median of per-step HIP events over graph replays, 1 GiB write between steps"},
+           "us_p10": round(p10, 3), "us_p90": round(p90, 3),
+           "warm_us": round(warm, 3),
+           "warm_note": "mean of back-to-back graph replays without the cache flush (weights may stay in the "
+                        "256 MB Infinity Cache)",
+           "bytes_per_layer_token": int(tb["total"]), "bytes_breakdown": {k: int(v) for k, v in tb.items()},
+           "achieved_GBps": round(gbps, 1), "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                        "kernel": "whole step (algorithmic bytes of every kernel / step time)"},
+           "dense": {"library_all_selected_us": round(dmed, 2), "torch_dense_layer_us": round(tmed, 2),
+                     "bytes": int(dbytes),
+                     "torch_launch": tmode,
+                     "note": "same flushed timing; torch: F.linear (hipBLASLt) projections + bmm attention"},
+           "speedup_vs_dense": round(min(dmed, tmed) / med, 3)}
+    del tfn, wsd, t, kc, vc
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_layer(w, log)
+    return out
+
+
+def timed_warm(step, n_steps):
+    """Mean time of back-to-back graph replays of `step` (no flush between them), in us."""
+    import torch
+    graph = torch.cuda.CUDAGraph()
+    step(0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step(0)
+    for i in range(3):
+        step(i)
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_steps):
+        step(i)
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n_steps
+
+
+def cpu_baseline_layer(w, log):
+    """The fp64 oracle on layer-tokens of a single-layer workload (predictor, top-k,
+    dense-with-mask layer), on every host core and then on one core (BLAS threads limited)."""
+    import numpy as np
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info, threadpool_limits
+    t = synth.layer_tensors(w, 0)
+    kc = synth.kv_cache(w, "k_cache", 0)
+    vc = synth.kv_cache(w, "v_cache", 0)
+
+    def one(step):
+        x = synth.x_input(w, step=step)
+        c0 = time.perf_counter()
+        s_m, s_h = oracle.predict(t["p1_mlp"], t["p2_mlp"], t["p1_head"], t["p2_head"], x)
+        S = oracle.topk(s_m.astype(np.float32), w.k)
+        Sh = oracle.topk(s_h.astype(np.float32), w.kh)
+        oracle.layer(x, t, kc, vc, w.t_past, S, Sh)
+        return time.perf_counter() - c0
+
+    res = {}
+    for label, limit in (("all_cores", None), ("one_core", 1)):
+        ctx = threadpool_limits(limits=limit) if limit else None
+        try:
+            if ctx is not None:
+                ctx.__enter__()
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            secs = []
+            while sum(secs) < 10.0 and len(secs) < 200:
+                secs.append(one(len(secs)))
+        finally:
+            if ctx is not None:
+                ctx.__exit__(None, None, None)
+        res[label] = {"value": round(float(np.median(secs)) * 1e6, 1), "unit": "us/layer-token", "cores": int(cores),
+                      "reps": len(secs)}
+        log(f"[bench] oracle {w.name} {label}: {res[label]}")
+    a = res["all_cores"]
+    return {"value": a["value"], "unit": "us/layer-token", "cores": a["cores"], "kind": "oracle",
+            "sample": f"{a['reps']} {w.name} layer-tokens (fresh x each, median reported): fp64 predictor + top-k + "
+                      f"dense-with-mask layer over all {w.d_ffn} neurons and {w.n_heads} heads, KV {w.t_past}",
+            "one_core": res["one_core"]}
 
 
 def run_batched(args, log):
@@ -455,10 +644,24 @@ def run_batched(args, log):
 
         dmed, _, _ = timed_single_layer(dstep, max(3, steps // 3), log)
         del wsd, ai, ah
+        # dense comparator in torch: hipBLASLt F.linear over the B rows, bmm attention
+        tfn = torch_dense_layer(w, lw, kc, vc, B)
+
+        def tstep(i):
+            if torch.cuda.is_current_stream_capturing():
+                y.copy_(tfn(x))
+            else:
+                x.copy_(xs[i % steps])
+
+        # hipBLASLt refuses stream capture on this image, so torch's layer is timed eagerly
+        tmed, _, _ = timed_single_layer(tstep, max(3, steps // 3), log, work=lambda: y.copy_(tfn(x)))
+        del tfn
         pt = {"batch": B, "union_neurons": nU, "union_heads": nUh, "us_per_step": round(med, 2),
               "us_p10": round(p10, 2), "us_p90": round(p90, 2), "us_per_token": round(med / B, 2),
               "bytes_per_step": int(tb["total"]), "achieved_GBps": round(tb["total"] / (med * 1e-6) / 1e9, 1),
-              "dense_us_per_step": round(dmed, 2), "speedup_vs_dense": round(dmed / med, 3)}
+              "dense_us_per_step": round(dmed, 2), "speedup_vs_dense": round(dmed / med, 3),
+              "torch_dense_us_per_step": round(tmed, 2), "speedup_vs_torch_dense": round(tmed / med, 3),
+              "speedup_vs_faster_dense": round(min(dmed, tmed) / med, 3)}
         log(f"[bench] batched B={B}: {pt}")
         points.append(pt)
         del ws, xs
@@ -468,6 +671,9 @@ def run_batched(args, log):
             "higher_is_better": False, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "opt175b-shaped layer, batch 1..32, Zipf(1.1) selections, KV 1024",
                        "k": w.k, "kh": w.kh, "rank": w.rank,
+                       "dense": "dense_us_per_step: this library with every neuron and head selected; "
+                                "torch_dense_us_per_step: torch F.linear (hipBLASLt) + bmm attention, same flushed "
+                                "timing but eager launches (hipBLASLt refuses stream capture)",
                        "timing": "median of per-step HIP events over graph replays, 1 GiB write between steps"},
             "points": points}
 
@@ -481,6 +687,7 @@ def run_sweep(args, log):
     from contextual_activation_sparsity_amd import traffic
     import synth
     import synth.device as sdev
+    import numpy as np
     w = synth.OPT66B_LAYER
     dims = dv.Dims(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.rank, w.t_max, w.dtype)
     t = sdev.layer_on_device(w, 0)
@@ -495,24 +702,29 @@ def run_sweep(args, log):
     x = torch.empty(1, w.d_model, device="cuda")
     y = torch.empty_like(x)
     points = []
-    for dm in synth.SWEEP_MLP:
-        for dhd in synth.SWEEP_HEAD:
-            k, kh = synth.count_at(dm, w.d_ffn), synth.count_at(dhd, w.n_heads)
-            ws = dv.workspace(dims, 1, k, kh)
+    cells = [(dm, dhd) for dm in synth.SWEEP_MLP for dhd in synth.SWEEP_HEAD]
+    if args.sweep_cells:
+        want = [tuple(float(v) for v in c.split(":")) for c in args.sweep_cells.split(",") if c.strip()]
+        cells = [c for c in cells if any(abs(c[0] - a) < 1e-9 and abs(c[1] - b) < 1e-9 for a, b in want)]
+        if len(cells) != len(want):
+            raise SystemExit(f"--sweep-cells must name cells of {synth.SWEEP_MLP} x {synth.SWEEP_HEAD}")
+    for dm, dhd in cells:
+        k, kh = synth.count_at(dm, w.d_ffn), synth.count_at(dhd, w.n_heads)
+        ws = dv.workspace(dims, 1, k, kh)
 
-            def step(i):
-                if torch.cuda.is_current_stream_capturing():
-                    dv.dv_layer_step(dims, lw, pw, x, x, k, kh, None, None, kc, vc, w.t_past, y, ws=ws)
-                else:
-                    x.copy_(xs[i % steps])
+        def step(i):
+            if torch.cuda.is_current_stream_capturing():
+                dv.dv_layer_step(dims, lw, pw, x, x, k, kh, None, None, kc, vc, w.t_past, y, ws=ws)
+            else:
+                x.copy_(xs[i % steps])
 
-            med, p10, p90 = timed_single_layer(step, steps, log)
-            tb = traffic.step_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.t_past, k, kh, 2)
-            pt = {"mlp_density": dm, "head_density": dhd, "k": k, "kh": kh, "us": round(med, 2),
-                  "us_p10": round(p10, 2), "us_p90": round(p90, 2), "bytes": int(tb["total"]),
-                  "achieved_GBps": round(tb["total"] / (med * 1e-6) / 1e9, 1)}
-            log(f"[bench] sweep {pt}")
-            points.append(pt)
+        med, p10, p90 = timed_single_layer(step, steps, log)
+        tb = traffic.step_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.rank, w.t_past, k, kh, 2)
+        pt = {"mlp_density": dm, "head_density": dhd, "k": k, "kh": kh, "us": round(med, 2),
+              "us_p10": round(p10, 2), "us_p90": round(p90, 2), "bytes": int(tb["total"]),
+              "achieved_GBps": round(tb["total"] / (med * 1e-6) / 1e9, 1)}
+        log(f"[bench] sweep {pt}")
+        points.append(pt)
     idx = torch.arange(w.d_ffn, dtype=torch.int32, device="cuda")[None].contiguous()
     heads = torch.arange(w.n_heads, dtype=torch.int32, device="cuda")[None].contiguous()
     wsd = dv.workspace(dims, 1, w.d_ffn, w.n_heads)
@@ -525,12 +737,56 @@ def run_sweep(args, log):
 
     dmed, _, _ = timed_single_layer(dstep, steps, log)
     dbytes = traffic.dense_layer_bytes(w.d_model, w.d_ffn, w.n_heads, w.head_dim, w.t_past, 2)
-    at5 = next(p for p in points if p["mlp_density"] == 0.05 and p["head_density"] == 0.20)
+    del wsd
+    # The same cells in lookahead mode, as the method runs them: a stack of L independent
+    # layers of this shape, the sets of layer l+1 predicted from the input of layer l on a side
+    # stream while layer l runs (layer 0's prediction is the only serial one). Timed over graph
+    # replays of the whole stack (L layers move far more than the Infinity Cache holds), fresh x
+    # copied in before each replay; us per layer-token = step / L.
+    L = max(2, args.sweep_layers)
+    layers, preds, kcs, vcs = [lw], [pw], [kc], [vc]
+    for l in range(1, L):
+        tl = sdev.layer_on_device(w, l)
+        layers.append(dv.LayerWeights(**{k: tl[k] for k in ("g1", "g2", "wqkv", "bqkv", "wo", "bo", "w1t", "b1",
+                                                              "w2", "b2")}))
+        preds.append(dv.PredictorWeights(**{k: tl[k] for k in ("p1_mlp", "p2_mlp", "p1_head", "p2_head")}))
+        kcs.append(sdev.kv_on_device(w, "k_cache", l))
+        vcs.append(sdev.kv_on_device(w, "v_cache", l))
+    side = torch.cuda.Stream()
+    for pt in points:
+        k, kh = pt["k"], pt["kh"]
+        sws = dv.stack_workspace(dims, 1, k, kh)
+        dv.dv_lookahead_stack(dims, layers, preds, x, k, kh, kcs, vcs, w.t_past, y, ws=sws, side_stream=side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dv.dv_lookahead_stack(dims, layers, preds, x, k, kh, kcs, vcs, w.t_past, y, ws=sws, side_stream=side)
+        ts = []
+        for i in range(steps + 2):
+            x.copy_(xs[i % steps])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e3 / L)
+        us = float(np.median(ts))
+        pt["lookahead_us"] = round(us, 2)
+        pt["lookahead_GBps"] = round(pt["bytes"] / (us * 1e-6) / 1e9, 1)
+        log(f"[bench] sweep lookahead mlp {pt['mlp_density']} head {pt['head_density']}: {us:.2f} us/layer-token")
+        del g, sws
+    del layers, preds, kcs, vcs
+    torch.cuda.empty_cache()
+    at5 = next((p for p in points if p["mlp_density"] == 0.05 and p["head_density"] == 0.20), points[0])
     return {"metric": "us per sparse decode layer-token over MLP x head density, OPT-66B shape",
             "value": at5["us"], "unit": "us/layer-token", "n_gpus": 1, "steps": steps, "higher_is_better": False,
             "dtype": "f32", "data": "synthetic",
             "config": {"workload": "opt66b-shaped layer density sweep, batch 1, inline prediction, KV 2048",
-                       "timing": "median of per-step HIP events over graph replays, 1 GiB write between steps"},
+                       "timing": "us: serial step (predictor, top-k, layer), median of per-step HIP events over "
+                                 "graph replays, 1 GiB write between steps; lookahead_us: the same cell in a stack "
+                                 f"of {L} layers with the next layer's prediction on a side stream, median "
+                                 "replay time / layers"},
             "dense": {"us": round(dmed, 2), "bytes": int(dbytes),
                       "achieved_GBps": round(dbytes / (dmed * 1e-6) / 1e9, 1)},
             "points": points}
