@@ -106,6 +106,10 @@ hipError_t launch_attn(const AttnArgs& a, bool f16, int B, hipStream_t s);
 // t[b] = min(t[b] + 1, cap) for b < B (per-row lengths after a decode step).
 hipError_t launch_advance_lengths(int32_t* t, int B, int cap, hipStream_t s);
 
+// The row-axpy's column-slice partials only (launch_axpy_reduce finishes them when RG > 1).
+hipError_t launch_rowaxpy_part(const RowAxpyArgs& a, bool f16, int tpc, int B, hipStream_t s);
+
+
 // ---------------------------------------------------------------------------
 // Exact top-k by radix select over many CUs (three kernels, see k_topk.hip).
 // ---------------------------------------------------------------------------

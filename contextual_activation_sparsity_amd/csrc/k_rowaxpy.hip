@@ -16,8 +16,7 @@
 //  2. rowaxpy_reduce_kernel: out = sum of the row groups' partials in group order + bias +
 //     resid. With a single row group the first kernel writes the output directly.
 // The sum order is fixed, so results are bitwise reproducible.
-#include "dv_device.h"
-#include "dv_kernels.h"
+#include "reduce_body.h"
 
 namespace dv {
 
@@ -33,7 +32,6 @@ namespace dv {
 constexpr int kAxpyBlock = 256;
 constexpr int kAxpyTpc = DV_AXPY_TPC;
 constexpr int kAxpyU = DV_AXPY_U;
-constexpr int kAxpyMaxRG = 32;
 constexpr int kAxpyStage = 1024;  // rows whose ids/coefficients are staged per sweep
 
 template <typename WT, int TPC>
@@ -139,23 +137,7 @@ __global__ __launch_bounds__(kAxpyBlock) void rowaxpy_part_kernel(RowAxpyArgs a)
 // thread, small blocks so the few hundred KB of partials are read by many CUs at once.
 constexpr int kReduceBlock = 64;
 __global__ __launch_bounds__(kReduceBlock) void rowaxpy_reduce_kernel(RowAxpyArgs a) {
-  const int b = blockIdx.y;
-  const int c0 = (blockIdx.x * kReduceBlock + threadIdx.x) * 4;
-  if (c0 >= a.d) return;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if (a.partial != nullptr) {   // no partials: bias + residual only
-    const float* p = a.partial + (long long)b * a.RG * a.d + c0;
-    f32x4 v[kAxpyMaxRG];
-#pragma unroll
-    for (int r = 0; r < kAxpyMaxRG; ++r)
-      if (r < a.RG) v[r] = *reinterpret_cast<const f32x4*>(p + (long long)r * a.d);
-#pragma unroll
-    for (int r = 0; r < kAxpyMaxRG; ++r)
-      if (r < a.RG) s += v[r];
-  }
-  if (a.bias) s += *reinterpret_cast<const f32x4*>(a.bias + c0);
-  if (a.resid) s += *reinterpret_cast<const f32x4*>(a.resid + (long long)b * a.ldr + c0);
-  *reinterpret_cast<f32x4*>(a.out + (long long)b * a.ldo + c0) = s;
+  axpy_reduce_block<kReduceBlock>(a, blockIdx.x, blockIdx.y);
 }
 
 int rowaxpy_max_rg() { return kAxpyMaxRG; }
@@ -176,12 +158,16 @@ void rowaxpy_plan(int d, int n_rows, bool f16, int B, int cus, int* tpc, int* n_
   *RG = (int)rg;
 }
 
-hipError_t launch_rowaxpy(const RowAxpyArgs& a, bool f16, int tpc, int B, hipStream_t s) {
+hipError_t launch_rowaxpy_part(const RowAxpyArgs& a, bool f16, int tpc, int B, hipStream_t s) {
   if (tpc != kAxpyTpc) return hipErrorInvalidValue;
   dim3 grid(a.n_slices, a.RG, B);
   if (f16) hipLaunchKernelGGL((rowaxpy_part_kernel<half_t, kAxpyTpc>), grid, dim3(kAxpyBlock), 0, s, a);
   else hipLaunchKernelGGL((rowaxpy_part_kernel<float, kAxpyTpc>), grid, dim3(kAxpyBlock), 0, s, a);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_rowaxpy(const RowAxpyArgs& a, bool f16, int tpc, int B, hipStream_t s) {
+  hipError_t e = launch_rowaxpy_part(a, f16, tpc, B, s);
   if (e != hipSuccess || a.RG == 1) return e;
   return launch_axpy_reduce(a, B, s);
 }
