@@ -140,9 +140,13 @@ __device__ __forceinline__ void attn_block(const AttnArgs& a, int c, int s, int 
 
 }
 
-// Combine the chunk partials of one (batch row, selected head): M = max m_c,
-// o = sum_c o_c e^(m_c - M) / sum_c l_c e^(m_c - M), in chunk order (deterministic). The
-// partials are staged in LDS with coalesced sweeps.
+// Combine the chunk partials of one (batch row, selected head):
+// o = sum_c o_c 2^(m_c - M) / sum_c l_c 2^(m_c - M) with M = max m_c (scores in the log2
+// domain), in chunk order (deterministic). The partials are staged in LDS with coalesced
+// sweeps of kAttnStage chunks, every load of a sweep issued before any is stored; the attention
+// plan keeps a head's chunks within one sweep where it can. Over several sweeps the sums are
+// kept relative to the running maximum and rescaled when a later sweep raises it, so every
+// partial is loaded once.
 template <int DH>
 __device__ __forceinline__ void attn_combine_block(const AttnArgs& a, int s, int b) {
   __shared__ float s_part[kAttnStage * (DH + 2)];
@@ -151,10 +155,9 @@ __device__ __forceinline__ void attn_combine_block(const AttnArgs& a, int s, int
   float* o = a.o + ((long long)b * a.kh + s) * DH;
   const int e = tid;
   float M = -INFINITY, L = 0.f, O = 0.f;
-  const bool one_sweep = a.n_chunks <= kAttnStage;
-  // all loads of a sweep are issued before any is stored
   constexpr int QMAX = (kAttnStage * (DH + 2) + kAttnBlock - 1) / kAttnBlock;
-  auto stage = [&](int c0, int nb) {
+  for (int c0 = 0; c0 < a.n_chunks; c0 += kAttnStage) {   // block-uniform
+    const int nb = min(kAttnStage, a.n_chunks - c0);
     const int n = nb * (DH + 2);
     const float* src = base + (long long)c0 * (DH + 2);
     float v[QMAX];
@@ -163,31 +166,29 @@ __device__ __forceinline__ void attn_combine_block(const AttnArgs& a, int s, int
       const int i = tid + q * kAttnBlock;
       v[q] = i < n ? src[i] : 0.f;
     }
-    __syncthreads();
+    __syncthreads();   // the previous sweep's readers are done
 #pragma unroll
     for (int q = 0; q < QMAX; ++q) {
       const int i = tid + q * kAttnBlock;
       if (i < n) s_part[i] = v[q];
     }
     __syncthreads();
-  };
-  for (int c0 = 0; c0 < a.n_chunks; c0 += kAttnStage) {
-    const int nb = min(kAttnStage, a.n_chunks - c0);
-    stage(c0, nb);
-    for (int cc = 0; cc < nb; ++cc) M = fmaxf(M, s_part[cc * (DH + 2)]);
-    if (one_sweep) break;
-  }
-  for (int c0 = 0; c0 < a.n_chunks; c0 += kAttnStage) {
-    const int nb = min(kAttnStage, a.n_chunks - c0);
-    if (!one_sweep) stage(c0, nb);
-    if (e < DH && M > -INFINITY) {
+    float Ms = M;
+    for (int cc = 0; cc < nb; ++cc) Ms = fmaxf(Ms, s_part[cc * (DH + 2)]);
+    if (e < DH && Ms > -INFINITY) {
+      if (M > -INFINITY && Ms > M) {   // a later sweep raised the maximum: rescale the sums
+        const float r = exp2f(M - Ms);
+        L *= r;
+        O *= r;
+      }
       for (int cc = 0; cc < nb; ++cc) {
         const float mc = s_part[cc * (DH + 2)];
-        const float f = (mc > -INFINITY) ? exp2f(mc - M) : 0.f;
+        const float f = (mc > -INFINITY) ? exp2f(mc - Ms) : 0.f;
         L = fmaf(s_part[cc * (DH + 2) + 1], f, L);
         O = fmaf(s_part[cc * (DH + 2) + 2 + e], f, O);
       }
     }
+    M = Ms;
   }
   if (e < DH) o[e] = (L > 0.f) ? O / L : 0.f;
 }

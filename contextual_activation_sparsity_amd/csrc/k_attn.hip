@@ -30,19 +30,26 @@ __global__ __launch_bounds__(kAttnBlock) void attn_combine_kernel(AttnArgs a) {
   attn_combine_block<DH>(a, blockIdx.x, blockIdx.y);
 }
 
+// Keys per block: the longest chunk (fewest partials) that still gives about two blocks per CU,
+// among chunkings whose partials fit one combine sweep; when none gives that many blocks, the
+// shortest chunk that fits one sweep (a latency-bound launch gains little from more blocks,
+// and a second sweep costs the combine a dependent round); when none fits, the longest chunk.
 bool attn_plan(int dh, bool f16, int t_total, int kh, int B, int cus, int* chunk, int* n_chunks) {
   const int vec = f16 ? 8 : 4;
   if (dh != 64 && dh != 128) return false;
   const int tpk = dh / vec;
   const int kpp = kAttnBlock / tpk;
   const long long want = 2LL * cus;
-  int npass = 2;
-  for (int np : {8, 4}) {
-    const long long nc = (t_total + kpp * np - 1) / (kpp * np);
-    if (nc * kh * B >= want) { npass = np; break; }
-  }
+  auto nc_of = [&](int np) { return (t_total + kpp * np - 1) / (kpp * np); };
+  int npass = 0;
+  for (int np : {8, 4, 2})
+    if ((long long)nc_of(np) * kh * B >= want && nc_of(np) <= kAttnStage) { npass = np; break; }
+  if (npass == 0)
+    for (int np : {2, 4, 8})
+      if (nc_of(np) <= kAttnStage) { npass = np; break; }
+  if (npass == 0) npass = 8;
   *chunk = kpp * npass;
-  *n_chunks = (t_total + *chunk - 1) / *chunk;
+  *n_chunks = nc_of(npass);
   return true;
 }
 

@@ -192,6 +192,34 @@ def test_sparse_attn(dv, host_layers, w, case):
                 assert np.array_equal(kg[b, h], kc[b, h]) and np.array_equal(vg[b, h], vc[b, h])
 
 
+@pytest.mark.parametrize("w", [W_RAG16, W_RAG32], ids=["ragged-f16", "ragged-f32"])
+@pytest.mark.parametrize("raise_late", [False, True], ids=["plain", "later-max"])
+def test_sparse_attn_long_cache_several_combine_sweeps(dv, host_layers, w, raise_late):
+    """A cache long enough that a head's chunk partials span two sweeps of the combine (over
+    5120 keys at 128 keys per block), at batch 2. With raise_late the keys past 5120 are
+    scaled up so the largest score sits in the second sweep and the first sweep's sums are
+    rescaled to it."""
+    t = host_layers[w.name]
+    B, T = 2, 6000
+    wc = batched(w, B).with_(t_past=T)
+    rng = np.random.default_rng(9)
+    Sh = random_sets(rng, B, w.n_heads, w.kh)
+    kc = kv_host(wc, "k_cache")
+    vc = kv_host(wc, "v_cache")
+    if raise_late:
+        kc = kc.copy()
+        kc[:, :, 5200:T] = (kc[:, :, 5200:T].astype(np.float32) * 3).astype(kc.dtype)
+    xn = xn_input(w, B, step=6)
+    dims = dims_of(wc)
+    d = to_dev({k_: t[k_] for k_ in ("wqkv", "bqkv", "wo", "bo", "w1t", "b1", "w2", "b2", "g1", "g2")})
+    y = torch.empty(B, w.d_model, device="cuda")
+    dv.dv_sparse_attn(dims, layer_weights(d), torch.from_numpy(xn).cuda(), torch.from_numpy(Sh).cuda(), w.kh,
+                      torch.from_numpy(kc).cuda(), torch.from_numpy(vc).cuda(), T, y, dv.workspace(dims, B, 0, w.kh))
+    torch.cuda.synchronize()
+    ref = oracle.attention(xn, t["wqkv"], t["bqkv"], t["wo"], t["bo"], kc, vc, T, oracle.masks_from_sets(Sh, w.n_heads))
+    assert_close(y.cpu().numpy(), ref["y_a"], w.dtype, f"y_a[T={T}, later max {raise_late}]", batch=B)
+
+
 # ---------------------------------------------------------------------------
 # layer step
 # ---------------------------------------------------------------------------
