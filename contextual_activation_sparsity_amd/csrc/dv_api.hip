@@ -49,41 +49,37 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t align256(size_t x) { return (x + 255u) & ~size_t(255u); }
 
+// Compute units of the current device (queried on every call: the library keeps no cache).
 struct DeviceInfo {
   int cus = 0;
-  hipEvent_t ev_in = nullptr, ev_sel[2] = {nullptr, nullptr};
 };
-// Fixed-size tables indexed by device ordinal: looking a device up never allocates.
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_cus[kMaxDevices];                 // compute units per device (0: not queried yet)
-thread_local DeviceInfo t_dev[kMaxDevices];          // the stack's fork/join events: per device and thread
 
-// Compute units of the current device and, with events, this thread's stack events on it.
-// Events are per thread so that stack calls from different host threads never record or
-// wait on each other's events.
-dv_status device_info(DeviceInfo** out, bool events) {
+dv_status device_info(DeviceInfo* out) {
   int dev = 0;
   DV_HIP(hipGetDevice(&dev));
-  if (dev < 0 || dev >= kMaxDevices) return fail(DV_ERR_HIP, "device ordinal %d beyond %d", dev, kMaxDevices);
-  DeviceInfo& di = t_dev[dev];
-  if (di.cus == 0) {
-    int cus = g_cus[dev].load(std::memory_order_relaxed);
-    if (cus == 0) {
-      int n = 0;
-      DV_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev));
-      cus = n > 0 ? n : 1;
-      g_cus[dev].store(cus, std::memory_order_relaxed);
-    }
-    di.cus = cus;
-  }
-  if (events && di.ev_in == nullptr) {
-    DV_HIP(hipEventCreateWithFlags(&di.ev_in, hipEventDisableTiming));
-    DV_HIP(hipEventCreateWithFlags(&di.ev_sel[0], hipEventDisableTiming));
-    DV_HIP(hipEventCreateWithFlags(&di.ev_sel[1], hipEventDisableTiming));
-  }
-  *out = &di;
+  int n = 0;
+  DV_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev));
+  out->cus = n > 0 ? n : 1;
   return DV_OK;
 }
+
+// The fork/join events of one stack call: created by the call and destroyed when it returns
+// (a recorded event may be destroyed before the work it marks has run; waits already queued on
+// it, or captured into a graph, are unaffected), so calls from different host threads never
+// share an event and nothing outlives the call.
+struct StackEvents {
+  hipEvent_t in = nullptr, sel[2] = {nullptr, nullptr};
+  ~StackEvents() {
+    for (hipEvent_t e : {in, sel[0], sel[1]})
+      if (e != nullptr) (void)hipEventDestroy(e);
+  }
+  dv_status create() {
+    DV_HIP(hipEventCreateWithFlags(&in, hipEventDisableTiming));
+    DV_HIP(hipEventCreateWithFlags(&sel[0], hipEventDisableTiming));
+    DV_HIP(hipEventCreateWithFlags(&sel[1], hipEventDisableTiming));
+    return DV_OK;
+  }
+};
 
 bool is_f16(const dv_dims* d) { return d->dtype == DV_F16; }
 int vec_of(const dv_dims* d) { return is_f16(d) ? 8 : 4; }
@@ -654,8 +650,9 @@ dv_status dv_predict(const dv_dims* dims, const dv_predictor* pred, const float*
   DV_TRY(check_ptr(s_head, "s_head"));
   const Layout L = layout_of(dims, B, 0, 0);
   DV_TRY(check_ws(ws, ws_bytes, L.total));
-  DeviceInfo* di;
-  DV_TRY(device_info(&di, false));
+  DeviceInfo dinfo;
+  DV_TRY(device_info(&dinfo));
+  const DeviceInfo* di = &dinfo;
   return run_predict(dims, pred, x_pred, B, s_mlp, s_head, L, ws, di->cus, stream);
 }
 
@@ -691,8 +688,9 @@ dv_status dv_sparse_mlp(const dv_dims* dims, const dv_layer* layer, const float*
   if (k > 0 && idx == nullptr) return fail(DV_ERR_NULL, "idx is NULL");
   const Layout L = layout_of(dims, B, k, 0);
   DV_TRY(check_ws(ws, ws_bytes, L.total));
-  DeviceInfo* di;
-  DV_TRY(device_info(&di, false));
+  DeviceInfo dinfo;
+  DV_TRY(device_info(&dinfo));
+  const DeviceInfo* di = &dinfo;
   if (batched(dims, B)) return run_mlp_batched(dims, layer, xn, nullptr, B, idx, k, y, nullptr, L, ws, di->cus, stream, false);
   return run_mlp(dims, layer, xn, nullptr, B, idx, k, y, nullptr, L, ws, di->cus, stream);
 }
@@ -731,8 +729,9 @@ dv_status dv_sparse_mlp_blocked(const dv_dims* dims, const dv_layer* layer, cons
   if (kb > 0 && blocks == nullptr) return fail(DV_ERR_NULL, "blocks is NULL");
   const Layout L = layout_of(dims, B, kb * bs, 0);
   DV_TRY(check_ws(ws, ws_bytes, L.total));
-  DeviceInfo* di;
-  DV_TRY(device_info(&di, false));
+  DeviceInfo dinfo;
+  DV_TRY(device_info(&dinfo));
+  const DeviceInfo* di = &dinfo;
   // whole blocks through the single-row gather kernels (rows of a block are contiguous)
   return run_mlp(dims, layer, xn, nullptr, B, blocks, kb, y, nullptr, L, ws, di->cus, stream, bs);
 }
@@ -752,8 +751,9 @@ dv_status dv_layer_labels(const dv_dims* dims, const dv_layer* layer, const floa
   const int D = dims->d_model, F = dims->d_ffn, H = dims->n_heads;
   const Layout L = layout_of(dims, B, F, H);
   DV_TRY(check_ws(ws, ws_bytes, L.total));
-  DeviceInfo* di;
-  DV_TRY(device_info(&di, false));
+  DeviceInfo dinfo;
+  DV_TRY(device_info(&dinfo));
+  const DeviceInfo* di = &dinfo;
   // the dense layer's attention block: every head of every row (row-wise kernels)
   int32_t* heads = at<int32_t>(ws, L.heads);
   DV_HIP(dv::launch_iota_rows(heads, B, H, stream));
@@ -864,8 +864,9 @@ dv_status dv_sparse_attn(const dv_dims* dims, const dv_layer* layer, const float
   if (kh > 0 && heads == nullptr) return fail(DV_ERR_NULL, "heads is NULL");
   const Layout L = layout_of(dims, B, 0, kh);
   DV_TRY(check_ws(ws, ws_bytes, L.total));
-  DeviceInfo* di;
-  DV_TRY(device_info(&di, false));
+  DeviceInfo dinfo;
+  DV_TRY(device_info(&dinfo));
+  const DeviceInfo* di = &dinfo;
   if (batched(dims, B))
     return run_attn_batched(dims, layer, xn, nullptr, B, heads, kh, k_cache, v_cache, KvLen{t_past, nullptr}, y, nullptr, L, ws,
                             di->cus, stream, nullptr, false);
@@ -892,8 +893,9 @@ dv_status dv_layer_step(const dv_dims* dims, const dv_layer* layer, const dv_pre
   }
   const Layout L = layout_of(dims, B, k, kh);
   DV_TRY(check_ws(ws, ws_bytes, L.total));
-  DeviceInfo* di;
-  DV_TRY(device_info(&di, false));
+  DeviceInfo dinfo;
+  DV_TRY(device_info(&dinfo));
+  const DeviceInfo* di = &dinfo;
   const int32_t* idx = idx_in;
   const int32_t* heads = heads_in;
   if (inline_pred) {
@@ -940,9 +942,10 @@ dv_status run_stack(const dv_dims* dims, const dv_layer* layers, const dv_predic
   const Layout L = layout_of(dims, B, k, kh);
   const size_t need = dv_stack_workspace_bytes(dims, B, k, kh);
   DV_TRY(check_ws(ws, ws_bytes, need));
-  DeviceInfo* di;
-  DV_TRY(device_info(&di, true));
-  const int cus = di->cus;
+  DeviceInfo dinfo;
+  DV_TRY(device_info(&dinfo));
+  const int cus = dinfo.cus;
+  StackEvents ev;
   const int D = dims->d_model;
 
   // carve: main layout, side layout, set rings, residual ping-pong
@@ -976,13 +979,14 @@ dv_status run_stack(const dv_dims* dims, const dv_layer* layers, const dv_predic
 
   const bool two = side_stream != stream;
   hipStream_t st_side = two ? side_stream : stream;
+  if (two) DV_TRY(ev.create());
   if (h_all) DV_HIP(hipMemcpyAsync(h_all, x, vecb, hipMemcpyDeviceToDevice, stream));
   // Layer 0's sets come from the stack input, before any layer runs.
   DV_TRY(run_predict(dims, &preds[0], h_in(0), B, at<float>(ws, L.s_mlp), at<float>(ws, L.s_head), L, ws, cus,
                      stream));
   DV_TRY(topk_sets(0, ws, stream));
   for (int l = 0; l < n_layers; ++l) {
-    if (two && l >= 1) DV_HIP(hipStreamWaitEvent(stream, di->ev_sel[l % 2], 0));
+    if (two && l >= 1) DV_HIP(hipStreamWaitEvent(stream, ev.sel[l % 2], 0));
     // The sets of layer l+1 are predicted from the input of layer l: predictor stage 1 reads
     // the same vector as layer l's q/k/v projection and rides in that launch; stage 2 and the
     // top-k then run on the side stream while layer l finishes.
@@ -991,10 +995,10 @@ dv_status run_stack(const dv_dims* dims, const dv_layer* layers, const dv_predic
     dv::RowDotSeg p1[2];
     if (fuse) predict_stage1_segs(dims, &preds[l + 1], h_in(l), at<float>(ws_side, L.z), p1);
     DV_TRY(run_layer(dims, &layers[l], h_in(l), B, sel_idx(l), k, sel_heads(l), kh, k_caches[l], v_caches[l],
-                     kv, h_outp(l), L, ws, cus, stream, (ahead && two) ? di->ev_in : nullptr,
+                     kv, h_outp(l), L, ws, cus, stream, (ahead && two) ? ev.in : nullptr,
                      fuse ? p1 : nullptr, fuse ? 2 : 0));
     if (ahead) {
-      if (two) DV_HIP(hipStreamWaitEvent(st_side, di->ev_in, 0));
+      if (two) DV_HIP(hipStreamWaitEvent(st_side, ev.in, 0));
       // Stage 2 is planned for three quarters of the CUs: it starts together with layer l's
       // attention, and a grid over every CU holds them all while attention waits (measured on
       // the 24-layer OPT-175B-shaped stack: 123.9 against 126.9 us per layer-token).
@@ -1005,7 +1009,7 @@ dv_status run_stack(const dv_dims* dims, const dv_layer* layers, const dv_predic
         DV_TRY(run_predict(dims, &preds[l + 1], h_in(l), B, at<float>(ws_side, L.s_mlp), at<float>(ws_side, L.s_head),
                            L, ws_side, cus, st_side));
       DV_TRY(topk_sets(l + 1, ws_side, st_side));
-      if (two) DV_HIP(hipEventRecord(di->ev_sel[(l + 1) % 2], st_side));
+      if (two) DV_HIP(hipEventRecord(ev.sel[(l + 1) % 2], st_side));
     }
   }
   if (advance) DV_HIP(dv::launch_advance_lengths(advance, B, dims->t_max - 1, stream));

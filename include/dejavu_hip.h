@@ -20,6 +20,10 @@
  *     allocates or frees device memory. Scratch space is the caller's workspace `ws`
  *     of at least dv_workspace_bytes(...) bytes (256-byte aligned); its contents need no
  *     initialisation and are garbage after the call.
+ *   - State the library keeps between calls: the device array that dv_layer_step_noalloc
+ *     uses as its workspace (with its per-device address), the thread's dv_last_error()
+ *     text, and the q/k/v timing hook while dv_timing_start is active. Nothing else: device
+ *     properties are queried per call and the stack's events live for one call.
  *   - Calls are asynchronous on `stream`; outputs are valid once the stream is synchronised
  *     or an event recorded after the call has completed. Two calls that share a workspace
  *     must be ordered (same stream, or an event between them).
@@ -194,8 +198,9 @@ dv_status dv_layer_step_noalloc(const dv_dims* dims, const dv_layer* layer, cons
  *   h_all (nullable) [n_layers+1][B][d]: receives every layer's input and the final output.
  *   idx_out [n_layers][B][k], heads_out [n_layers][B][kh] (nullable): the sets used.
  *   side_stream may equal stream (then everything is serial). Results are bitwise identical
- *   either way. Workspace: dv_stack_workspace_bytes(). Events are created once per device
- *   and thread and kept for the life of the process. */
+ *   either way. Workspace: dv_stack_workspace_bytes(). The call creates its own fork/join
+ *   events and destroys them before returning (also under stream capture: the captured
+ *   graph keeps the dependencies, not the events). */
 dv_status dv_lookahead_stack(const dv_dims* dims, const dv_layer* layers, const dv_predictor* preds,
                              int32_t n_layers, const float* x, int32_t B, int32_t k, int32_t kh,
                              void* const* k_caches, void* const* v_caches, int32_t t_past,
