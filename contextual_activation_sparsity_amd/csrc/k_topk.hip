@@ -15,7 +15,9 @@
 //     straight into a bitmap of selected positions) and "in d0" (candidates, compacted in
 //     index order into the chunk's list).
 //  Problems of at most 256 scores (the heads) are selected whole by one block of the first
-//  launch (rank by counting), and the other two kernels skip them.
+//  launch (rank by counting), and the other two kernels skip them. When no problem of the
+//  launch has more than 16384 scores, one block per row selects each problem whole instead
+//  (topk_single_kernel: the same radix passes over keys held in registers), in one launch.
 //  3. topk_finish_kernel: one block per row gathers the candidates (typically 1-3 % of n),
 //     resolves the remaining 21 key bits with two more histogram passes, takes the ties at
 //     the threshold key in index order, sets their bits, and turns the bitmap into the
@@ -373,6 +375,103 @@ __global__ __launch_bounds__(kTkBlock) void topk_finish_kernel(TopkArgs a) {
   }
 }
 
+// Problems of at most kTkSingle scores (and more than kTkSmall) are selected whole by one
+// block per row, in one launch: thread t holds the keys of the EPT consecutive positions from
+// EPT*t in registers; three histogram passes over their 11/11/10-bit digits (each pass counts
+// only the keys that share the digits found so far) find tau, the k-th largest key, and how
+// many keys equal to tau are taken. A block scan of the per-thread counts of tau-keys gives each
+// thread the ties at lower positions (the lower index wins), and a scan of the per-thread
+// selected counts places each thread's picks in the ascending list. Same keys, same tie rule.
+constexpr int kTkSingle = 16384;   // measured: at 36864 scores the three launches over many CUs win
+
+template <int EPT>
+__global__ __launch_bounds__(kTkBlock) void topk_single_kernel(TopkArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned s_hist[kTkBins];
+  __shared__ unsigned s_scan[kTkWaves];
+  __shared__ unsigned s_sel[3];
+  static_assert(EPT * kTkBlock >= kTkSingle, "the largest single-block problem fits");
+  const TopkProb& P = prob_of(a);
+  const int b = blockIdx.x, n = P.n, k = P.k, tid = threadIdx.x;
+  if (k <= 0) return;
+  if (n <= kTkSmall) {   // block-uniform
+    topk_small(P, b, s_hist, s_scan);
+    return;
+  }
+  int32_t* out = P.out + (long long)b * k;
+  if (k >= n) {
+    for (int i = tid; i < n; i += kTkBlock) out[i] = i;
+    return;
+  }
+  const float* sc = P.scores + (long long)b * n;
+  const int i0 = tid * EPT;
+  unsigned key[EPT];
+  if ((EPT % 4) == 0 && (reinterpret_cast<uintptr_t>(sc) & 15u) == 0 && i0 + EPT <= n) {
+#pragma unroll
+    for (int j = 0; j < EPT; j += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sc + i0 + j);
+      key[j] = order_key(v[0]); key[j + 1] = order_key(v[1]);
+      key[j + 2] = order_key(v[2]); key[j + 3] = order_key(v[3]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) key[j] = i0 + j < n ? order_key(sc[i0 + j]) : 0u;
+  }
+  const int nv = max(0, min(EPT, n - i0));   // valid positions of this thread
+  unsigned krem = (unsigned)k, prefix = 0u, pmask = 0u;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    const unsigned dmask = (unsigned)nb - 1u;
+    for (int i = tid; i < kTkBins; i += kTkBlock) s_hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+      if (j < nv && (key[j] & pmask) == prefix) atomicAdd(&s_hist[(key[j] >> shift) & dmask], 1u);
+    __syncthreads();
+    const int b0 = nb - 1 - 2 * tid, b1 = nb - 2 - 2 * tid;
+    const unsigned h0 = b0 >= 0 ? s_hist[b0] : 0u;
+    const unsigned h1 = b1 >= 0 ? s_hist[b1] : 0u;
+    select_bin(h0, h1, nb, krem, s_sel, s_scan);
+    prefix |= s_sel[0] << shift;
+    pmask |= dmask << shift;
+    krem = s_sel[1];
+  }
+  const unsigned tau = prefix, take = krem;   // take of the keys equal to tau, lowest positions first
+  unsigned ne = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) ne += (j < nv && key[j] == tau) ? 1u : 0u;
+  unsigned tot;
+  unsigned eq_seen = block_scan(ne, &tot, s_scan);   // tau-keys at lower positions
+  unsigned cnt = 0;
+  unsigned selbits = 0u;   // bit j: position i0 + j is selected
+  static_assert(EPT <= 32, "one word of selection bits per thread");
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    bool on = false;
+    if (j < nv) {
+      if (key[j] > tau) {
+        on = true;
+      } else if (key[j] == tau) {
+        on = eq_seen < take;
+        ++eq_seen;
+      }
+    }
+    if (on) {
+      ++cnt;
+      selbits |= 1u << j;
+    }
+  }
+  unsigned pos = block_scan(cnt, &tot, s_scan);
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    if ((selbits >> j) & 1u) {
+      if (pos < (unsigned)k) out[pos] = i0 + j;   // always true for a correct selection
+      ++pos;
+    }
+  }
+}
+
 size_t topk_ws_bytes(int B, int n) {
   const size_t nch = (size_t)((n + kTopkChunk - 1) / kTopkChunk);
   const size_t per_row = nch * kTkBins        // part
@@ -406,6 +505,11 @@ hipError_t launch_topk(const TopkArgs& a, int B, hipStream_t s) {
   for (int i = 0; i < a.nprob; ++i) {
     if (a.p[i].n > kTopkMaxChunks * kTopkChunk) return hipErrorInvalidValue;
     nmax = max(nmax, a.p[i].n);
+  }
+  if (nmax > kTkSmall && nmax <= kTkSingle) {   // one block per row and problem, one launch
+    const dim3 g1(B, 1, a.nprob);
+    hipLaunchKernelGGL(topk_single_kernel<kTkSingle / kTkBlock>, g1, dim3(kTkBlock), 0, s, a);
+    return hipGetLastError();
   }
   const int nch = (nmax + kTopkChunk - 1) / kTopkChunk;
   const dim3 grid(nch, B, a.nprob);
