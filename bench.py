@@ -205,6 +205,14 @@ def main() -> int:
                      "p90": round(float(np.percentile(per, 90)), 3), "replays": len(per)}
         log(f"[bench] per-replay us/layer-token: {step_dist}")
 
+    # (2b) where the time goes, each as a captured graph replayed back to back: the layers alone
+    #      with their sets given (the main chain), the predictions alone (the side chain: both
+    #      stage-1 factors, stage 2 and the top-k of every layer), and the whole step with the
+    #      predictions on the main stream (serial)
+    split = None
+    if not args.no_graph:
+        split = time_split(dv, w, dims, layers, preds, kcs, vcs, xs, ws, y, args, log)
+
     # (3) eager again with HIP event pairs around every q/k/v gather launch (on its stream)
     n_ev = args.steps * L
     assert _lib.lib().dv_timing_start(n_ev) == n_ev
@@ -271,6 +279,7 @@ def main() -> int:
                      "launches_timed": int(n_ev), "stream_read_GBps": round(stream_read, 1),
                      "frac_of_stream_read": round(qkv_gbps / stream_read, 4)},
         "us_per_layer_token_per_replay": step_dist,
+        "time_split_us_per_layer_token": split,
         "step_pct_of_stream_read": round(100.0 * gbps / stream_read, 2),
     }
 
@@ -285,6 +294,72 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(w, log)
     print(json.dumps(out), flush=True)
     return 0
+
+
+def time_split(dv, w, dims, layers, preds, kcs, vcs, xs, ws, y, args, log):
+    """Per layer-token: the main chain alone (every layer's sets given, taken from one stack
+    run), the side chain alone (predictor and top-k of every layer), the serial step (one
+    stream) and the two-stream step, each captured once and replayed back to back."""
+    import torch
+    L = len(layers)
+    io = torch.empty(L, 1, w.k, dtype=torch.int32, device="cuda")
+    ho = torch.empty(L, 1, w.kh, dtype=torch.int32, device="cuda")
+    x_in = torch.empty(1, w.d_model, device="cuda")
+    x_in.copy_(xs[0])
+    dv.dv_lookahead_stack(dims, layers, preds, x_in, w.k, w.kh, kcs, vcs, w.t_past, y, idx_out=io, heads_out=ho,
+                          ws=ws)
+    lws = dv.workspace(dims, 1, w.k, w.kh)
+    h = torch.empty(1, w.d_model, device="cuda")
+    s_m = torch.empty(1, w.d_ffn, device="cuda")
+    s_h = torch.empty(1, w.n_heads, device="cuda")
+    pi = torch.empty(1, w.k, dtype=torch.int32, device="cuda")
+    ph = torch.empty(1, w.kh, dtype=torch.int32, device="cuda")
+    tws_m = torch.empty(dv.dv_topk_workspace_bytes(1, w.d_ffn), dtype=torch.uint8, device="cuda")
+    tws_h = torch.empty(dv.dv_topk_workspace_bytes(1, w.n_heads), dtype=torch.uint8, device="cuda")
+
+    def main_chain():
+        h.copy_(x_in)
+        for l in range(L):
+            dv.dv_layer_step(dims, layers[l], None, h, None, w.k, w.kh, io[l], ho[l], kcs[l], vcs[l], w.t_past, h,
+                             ws=lws)
+
+    def side_chain():
+        for l in range(L):
+            dv.dv_predict(dims, preds[l], x_in, s_m, s_h, lws)
+            dv.dv_topk(s_m, w.k, pi, tws_m)
+            dv.dv_topk(s_h, w.kh, ph, tws_h)
+
+    def serial():
+        dv.dv_lookahead_stack(dims, layers, preds, x_in, w.k, w.kh, kcs, vcs, w.t_past, y, ws=ws)
+
+    side = torch.cuda.Stream()
+
+    def two_stream():
+        dv.dv_lookahead_stack(dims, layers, preds, x_in, w.k, w.kh, kcs, vcs, w.t_past, y, ws=ws, side_stream=side)
+
+    out = {}
+    n = max(20, min(args.steps, 100))
+    for name, fn in (("main_chain_alone", main_chain), ("side_chain_alone", side_chain), ("serial", serial),
+                     ("two_streams", two_stream)):
+        fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(3):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) * 1e3 / n / L, 2)
+        del g
+    log(f"[bench] time split (us per layer-token): {out}")
+    del lws, tws_m, tws_h
+    return out
 
 
 def dense_baselines(dv, w, dims, layers, kcs, vcs, xs, n_steps, log):
