@@ -454,6 +454,12 @@ static_assert(DV_ROWS_DYN_MAXB <= 16, "the device-side split launches the 16-row
 #define DV_COLS_CW 256   // output columns per block: 512-byte strips of every weight row
 #endif
 
+// LDS slot of tile column c: columns are rotated within each group of 8 by half the group
+// number, so that the 16-byte transposed writes of 16 neighbouring lanes (columns 8 apart) and
+// the B-fragment reads of 16 neighbouring columns each fall on 16 distinct bank quads with the
+// 36-dword column pitch (the plain layout put 8 lanes on each quad of the writes).
+__device__ __forceinline__ int cols_slot(int c) { return (c & ~7) | (((c & 7) + (c >> 4)) & 7); }
+
 // A tile is KT gathered rows x CW columns (32 KB). Each thread loads the same 8 columns of 8
 // consecutive rows (for a fixed row, a wave reads CW/8*16 contiguous bytes per row), transposes
 // that 8 x 8 block in registers and writes each column's 8 rows as one 16-byte LDS store: the
@@ -547,7 +553,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
       for (int q = 0; q < 8; ++q) colv8[j][q] = __builtin_bit_cast(h8v, cur[q])[j];
     __syncthreads();   // the previous tile's readers are done
 #pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<h8v*>(&s_w[(8 * tc + j) * LDK + 8 * trg]) = colv8[j];
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<h8v*>(&s_w[cols_slot(8 * tc + j) * LDK + 8 * trg]) = colv8[j];
     if (cb < MT * 16) *reinterpret_cast<h8v*>(&s_c[cb * LDK + ck]) = ccur;
     __syncthreads();
 #pragma unroll
@@ -555,7 +561,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
 #pragma unroll
       for (int i = 0; i < CTW; ++i) {
         const int cl = (wv * CTW + i) * 16 + lr;
-        const h8v bf = *reinterpret_cast<const h8v*>(&s_w[cl * LDK + 32 * kstep + 8 * lg]);
+        const h8v bf = *reinterpret_cast<const h8v*>(&s_w[cols_slot(cl) * LDK + 32 * kstep + 8 * lg]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const h8v af = *reinterpret_cast<const h8v*>(&s_c[(16 * mt + lr) * LDK + 32 * kstep + 8 * lg]);
