@@ -460,6 +460,8 @@ static_assert(DV_ROWS_DYN_MAXB <= 16, "the device-side split launches the 16-row
 // 36-dword column pitch (the plain layout put 8 lanes on each quad of the writes).
 __device__ __forceinline__ int cols_slot(int c) { return (c & ~7) | (((c & 7) + (c >> 4)) & 7); }
 
+constexpr int kColsRowStage = 2048;   // union positions whose weight rows are staged in LDS per sweep
+
 // A tile is KT gathered rows x CW columns (32 KB). Each thread loads the same 8 columns of 8
 // consecutive rows (for a fixed row, a wave reads CW/8*16 contiguous bytes per row), transposes
 // that 8 x 8 block in registers and writes each column's 8 rows as one 16-byte LDS store: the
@@ -476,6 +478,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
   static_assert(KT % 32 == 0 && CTW >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) half_t s_w[CW * LDK];
   __shared__ __attribute__((aligned(16))) _Float16 s_c[MT * 16 * LDK];   // coefficients [b][k] of the tile
+  __shared__ int s_rows[kColsRowStage];   // weight rows of the staged sweep of union positions
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int lr = lane % 16, lg = lane / 16;
   const int tc = tid % TPC, trg = tid / TPC;
@@ -496,11 +499,27 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
     if ((unsigned)grp >= (unsigned)a.n_groups) return -1;
     return grp * a.G + (k - g * a.G);
   };
-  // Row numbers of a tile come from the union list; they are fetched two tiles ahead, before
-  // the weight loads of the tile in between, so waiting for them never waits for weights.
-  auto rows_for = [&](int* r, int kb) {
+  // The weight rows of the group's union positions are staged in LDS a sweep of
+  // kColsRowStage positions at a time (every index load of the sweep in flight together), so
+  // the tile loop takes them from LDS instead of waiting on a dependent global load per tile.
+  int sweep0 = kb0;
+  auto stage_rows = [&](int k0) {   // block-uniform; k0 is a tile boundary
+    constexpr int PT = kColsRowStage / kGemmBlock;
+    int v[PT];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) r[q] = row_of(kb + 8 * trg + q);
+    for (int q = 0; q < PT; ++q) v[q] = row_of(k0 + tid + q * kGemmBlock);
+    __syncthreads();   // the previous sweep's readers are done
+#pragma unroll
+    for (int q = 0; q < PT; ++q) s_rows[tid + q * kGemmBlock] = v[q];
+    __syncthreads();
+    sweep0 = k0;
+  };
+  auto rows_for = [&](int* r, int kb) {   // the tile at kb lies in the staged sweep
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int k = kb + 8 * trg + q;
+      r[q] = k < kend ? s_rows[k - sweep0] : -1;
+    }
   };
   auto load_tile = [&](u32x4* wt, const int* r) {
 #pragma unroll
@@ -533,18 +552,20 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
     for (int mt = 0; mt < MT; ++mt) acc[i][mt] = f4v{0.f, 0.f, 0.f, 0.f};
   u32x4 cur[8], nxt[8];
   h8v ccur, cnxt;
-  int rn[8], rnn[8];
+  int rn[8];
   if (kb0 < kend) {
+    stage_rows(kb0);
     rows_for(rn, kb0);
     load_tile(cur, rn);
     load_coef(ccur, kb0);
-    rows_for(rn, kb0 + KT);
   }
   for (int kb = kb0; kb < kend; kb += KT) {   // block-uniform
-    rows_for(rnn, kb + 2 * KT);   // no loads past the group's end (row_of returns -1 there)
-    if (kb + KT < kend) {
+    const int kn = kb + KT;
+    if (kn < kend) {
+      if (kn >= sweep0 + kColsRowStage) stage_rows(kn);
+      rows_for(rn, kn);   // no loads past the group's end (rows_for gives -1 there)
       load_tile(nxt, rn);
-      load_coef(cnxt, kb + KT);
+      load_coef(cnxt, kn);
     }
     h8v colv8[8];
 #pragma unroll
@@ -569,10 +590,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm_cols_kernel(GemmColsArgs a) {
         }
       }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      cur[q] = nxt[q];
-      rn[q] = rnn[q];
-    }
+    for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
     ccur = cnxt;
   }
   // D layout: lane holds output column lr of its tile, batch rows 16*mt + 4*lg + e
