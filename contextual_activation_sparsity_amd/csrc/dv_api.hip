@@ -143,7 +143,7 @@ dv_status check_pred(const dv_predictor* P) {
 struct Layout {
   size_t z, s_mlp, s_head, idx, heads, qkv, apart, o, h1, u, part, tk_mlp, tk_head, kpart, total;
   // batched path (B >= 2): union bitmaps and lists, fp16 operands
-  size_t ubits, hbits, ulist, uhlist, counts, ucnt, xh, xl, zh, zl, cu, co;
+  size_t ubits, hbits, ulist, uhlist, counts, ucnt, xh, zh, zl, cu, co;
   int max_u, max_uh;
   int max_chunks;
 };
@@ -181,7 +181,6 @@ Layout layout_of(const dv_dims* d, int B, int k, int kh) {
     L.counts = take(4 * 4);
     L.ucnt = take(4 * 2 * (size_t)(dv::kUnionMaxN / 32 / dv::kUnionWpb));
     L.xh = take(2 * Bz * d->d_model);
-    L.xl = take(2 * Bz * d->d_model);
     L.zh = take(2 * Bz * (d->rank_mlp + d->rank_head));
     L.zl = take(2 * Bz * (d->rank_mlp + d->rank_head));
     L.cu = take(2 * Bz * (size_t)L.max_u);
@@ -278,15 +277,13 @@ dv::GemmRowsArgs rows_args(const void* W, long long ld, int dlen, const int32_t*
 dv_status run_predict_batched(const dv_dims* d, const dv_predictor* P, const float* x, int B, float* s_mlp,
                               float* s_head, const Layout& L, void* ws, int cus, hipStream_t st) {
   const int rm = d->rank_mlp, rh = d->rank_head, D = d->d_model;
-  _Float16* xh = at<_Float16>(ws, L.xh);
-  _Float16* xl = at<_Float16>(ws, L.xl);
   _Float16* zh = at<_Float16>(ws, L.zh);
   _Float16* zl = at<_Float16>(ws, L.zl);
-  DV_HIP(dv::launch_rows_norm_f16(x, D, nullptr, D, 0.f, B, xh, xl, D, st));
-  // both stage-1 factors in one launch: rows [0, rm) of P1_mlp, then rows of P1_head (z = [z_m; z_h])
-  dv::GemmRowsArgs a = rows_args(P->p1_mlp, D, D, nullptr, nullptr, 1, rm + rh, B, xh, D, at<float>(ws, L.kpart));
+  // both stage-1 factors in one launch: rows [0, rm) of P1_mlp, then rows of P1_head (z = [z_m; z_h]);
+  // x enters in fp32 and is split into an fp16 part and its remainder as it is staged
+  dv::GemmRowsArgs a = rows_args(P->p1_mlp, D, D, nullptr, nullptr, 1, rm + rh, B, nullptr, D, at<float>(ws, L.kpart));
   a.W_b = P->p1_head; a.n_rows_a = rm;
-  a.X_lo = xl; a.mode = dv::kGemmOutF16; a.outh = zh; a.outh_lo = zl; a.ldo = rm + rh;
+  a.Xf = x; a.mode = dv::kGemmOutF16; a.outh = zh; a.outh_lo = zl; a.ldo = rm + rh;
   DV_HIP(dv::launch_gemm_rows(a, rm + rh, cus, st));
   a.W_b = nullptr; a.n_rows_a = 0;
   a = rows_args(P->p2_mlp, rm, rm, nullptr, nullptr, 1, d->d_ffn, B, zh, rm + rh, at<float>(ws, L.kpart));

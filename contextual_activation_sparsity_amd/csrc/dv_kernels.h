@@ -178,6 +178,8 @@ struct GemmRowsArgs {                // out[b][i] = act(W[row_i] . X[b] + bias[r
   int B;
   const _Float16* X;                 // [B][ldx]
   const _Float16* X_lo;              // nullable: rounding remainders of X (same layout)
+  const float* Xf;                   // nullable: fp32 activations [B][ldx] instead of X and X_lo, split
+                                     //   into an fp16 part and its fp16 remainder as they are staged
   long long ldx;
   const float* bias;                 // nullable
   int relu;

@@ -304,10 +304,13 @@ __device__ __forceinline__ void rows_store(const GemmRowsArgs& a, int i, int b, 
 // wave covers 2 rows x 512 contiguous bytes, and the activation rows (and their remainders)
 // are staged once per block instead of once per wave. The next chunk's loads are in flight
 // while the MFMAs consume the current one. No cross-wave sum: each wave owns its rows.
+// With XF the activations come as fp32 and are split into an fp16 part and its fp16
+// remainder while they are staged (the same bits a separate conversion pass would write).
 constexpr int kRowsKC = 256;
 constexpr int kRowsLdk = kRowsKC + 8;
-template <int NT, bool SPLIT>
+template <int NT, bool SPLIT, bool XF = false>
 __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
+  static_assert(SPLIT || !XF, "fp32 activations are staged as a part and its remainder");
   constexpr int NX = NT * 16;                   // staged activation rows
   constexpr int XL = SPLIT ? 2 : 1;
   constexpr int XLD = NX * kRowsKC / 8 / 256;   // 16-byte activation loads per thread per array
@@ -356,6 +359,7 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
   const _Float16* XLs = second ? a.X_lo_b : a.X_lo;
   u32x4 wreg[8];
   h8v xreg[XL][XLD];
+  f32x4 xraw[XF ? XLD : 1][2];   // XF: the fp32 activations of the chunk in flight
   auto load = [&](int k0) {
     const bool kok = k0 + kk < a.d;   // d is a multiple of 8: a chunk is wholly in or out
 #pragma unroll
@@ -366,10 +370,17 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
     for (int p = 0; p < XLD; ++p) {
       const int b = lrow + 8 * p;
       const bool ok = kok && b < a.B;
-      xreg[0][p] = ok ? *reinterpret_cast<const h8v*>(Xs + (long long)b * a.ldx + k0 + kk) : h8v{0, 0, 0, 0, 0, 0, 0, 0};
-      if constexpr (SPLIT)
-        xreg[1][p] = ok ? *reinterpret_cast<const h8v*>(XLs + (long long)b * a.ldx + k0 + kk)
+      if constexpr (XF) {
+        const float* xp = a.Xf + (long long)b * a.ldx + k0 + kk;
+        xraw[p][0] = ok ? *reinterpret_cast<const f32x4*>(xp) : f32x4{0.f, 0.f, 0.f, 0.f};
+        xraw[p][1] = ok ? *reinterpret_cast<const f32x4*>(xp + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        xreg[0][p] = ok ? *reinterpret_cast<const h8v*>(Xs + (long long)b * a.ldx + k0 + kk)
                         : h8v{0, 0, 0, 0, 0, 0, 0, 0};
+        if constexpr (SPLIT)
+          xreg[1][p] = ok ? *reinterpret_cast<const h8v*>(XLs + (long long)b * a.ldx + k0 + kk)
+                          : h8v{0, 0, 0, 0, 0, 0, 0, 0};
+      }
     }
   };
   f4v acc[NT];
@@ -384,6 +395,17 @@ __global__ __launch_bounds__(256) void gemm_rows_lds_kernel(GemmRowsArgs a) {
     __syncthreads();   // the previous chunk's readers are done
 #pragma unroll
     for (int q = 0; q < 8; ++q) *reinterpret_cast<u32x4*>(&s_w[(lrow + 8 * q) * kRowsLdk + kk]) = wreg[q];
+    if constexpr (XF) {
+#pragma unroll
+      for (int p = 0; p < XLD; ++p)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = xraw[p][e / 4][e % 4];
+          const _Float16 hi = static_cast<_Float16>(v);
+          xreg[0][p][e] = hi;
+          xreg[1][p][e] = static_cast<_Float16>(v - static_cast<float>(hi));
+        }
+    }
 #pragma unroll
     for (int x = 0; x < XL; ++x)
 #pragma unroll
@@ -646,7 +668,9 @@ hipError_t launch_rows_norm_f16(const float* x, long long ldx, const float* g, i
 
 template <int NT, bool SPLIT>
 static void launch_rows_lds(const GemmRowsArgs& a, int max_rows, int ks, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_rows_lds_kernel<NT, SPLIT>), dim3((max_rows + 63) / 64, ks), dim3(256), 0, s, a);
+  if (SPLIT && a.Xf != nullptr)
+    hipLaunchKernelGGL((gemm_rows_lds_kernel<NT, SPLIT, SPLIT>), dim3((max_rows + 63) / 64, ks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((gemm_rows_lds_kernel<NT, SPLIT>), dim3((max_rows + 63) / 64, ks), dim3(256), 0, s, a);
 }
 
 // A short launch (fewer 64-row tiles than twice the CUs) splits K over blocks, up to
@@ -658,8 +682,9 @@ hipError_t launch_gemm_rows(const GemmRowsArgs& a_in, int max_rows, int cus, hip
     return hipErrorInvalidValue;
   if (a.X_b != nullptr && (a.W_b == nullptr || a.n_rows_a % 64 != 0 || (a.X_lo != nullptr) != (a.X_lo_b != nullptr)))
     return hipErrorInvalidValue;
+  if (a.Xf != nullptr && (a.X_b != nullptr || a.X_lo != nullptr)) return hipErrorInvalidValue;
   if (max_rows == 0) return hipSuccess;
-  const bool split = a.X_lo != nullptr;
+  const bool split = a.X_lo != nullptr || a.Xf != nullptr;
   const int tiles = (max_rows + 63) / 64;
   const int nch = (a.d + kRowsKC - 1) / kRowsKC;
   int ks = 1;
