@@ -266,3 +266,35 @@ def test_opt175b_batched_full_size_sampled_rows(dv, B):
                 assert np.max(np.abs(slot - r)) <= BATCHED_BAR * 4 * max(rms(r), 1e-30) + 2 ** -10 * np.max(np.abs(r))
     del t, kc, vc, ws
     torch.cuda.empty_cache()
+
+@pytest.mark.timeout(900)
+def test_opt175b_batched_every_neuron_two_row_sweeps(dv):
+    """The OPT-175B-shaped layer at B = 3 with every neuron selected: the union holds all
+    49152 neurons, so each row group of the down-projection spans 3072 union positions and
+    its weight-row numbers are staged in LDS in two sweeps (2048, then 1024 positions); the
+    up-projections split K on the device over 768 tiles. Row 1 is checked against the oracle
+    on its regenerated rows (output and MLP part)."""
+    import synth.device as sdev
+    from helpers import oracle_layer_compact
+    w = synth.OPT175B_BATCHED.with_(batch=3, k=49152)
+    B = w.batch
+    dims = dims_of(w)
+    t = sdev.layer_on_device(w, 0)
+    kc = sdev.kv_on_device(w, "k_cache", 0)
+    vc = sdev.kv_on_device(w, "v_cache", 0)
+    S = np.tile(np.arange(w.d_ffn, dtype=np.int32), (B, 1))
+    Sh = zipf_sets(w, B, w.n_heads, w.kh, "sel_head")
+    x = synth.x_input(w, step=2)
+    xd = torch.from_numpy(x).cuda()
+    out = torch.empty_like(xd)
+    ws = dv.workspace(dims, B, w.k, w.kh)
+    dv.dv_layer_step(dims, layer_weights(t), None, xd, None, w.k, w.kh, torch.from_numpy(S).cuda(),
+                     torch.from_numpy(Sh).cuda(), kc, vc, w.t_past, out, ws=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del t, kc, vc, ws
+    torch.cuda.empty_cache()
+    b = 1
+    ref = oracle_layer_compact(w, 0, x[b], S[b], Sh[b], b)
+    close(got[b:b + 1], ref["out"], f"row {b} layer out")
+    close(got[b:b + 1] - ref["h1"], ref["y_m"], f"row {b} y_m")
