@@ -16,12 +16,14 @@
 //    instruction); a wave owns 16 rows, fp32 accumulation with v_mfma_f32_16x16x32_f16.
 //    With a low part X_lo the product is taken twice (W . X_hi + W . X_lo): the fp16 weights
 //    are exact, so the result then carries fp32-like activation precision (used for the
-//    predictor's scores). Short launches split K over blocks and add the slices in order.
+//    predictor's scores; its first factor takes the fp32 input and splits it into the two
+//    parts while staging it). Short launches split K over blocks and add the slices in order.
 //  * gemm_cols (down-projection, Wo and W2): partial[b][rg][c] = sum over the rows of row
 //    group rg of C[b][k] * W[row_k][c]. Weight rows are read in 512-byte strips, transposed
 //    8 x 8 in registers and staged in LDS so each lane's B fragment (8 consecutive k at one
-//    column) is one 16-byte LDS read. The row groups are summed by the ordered reduce kernel
-//    of the gather-axpy.
+//    column) is one 16-byte LDS read. The weight rows of a block's union positions are
+//    staged in LDS a sweep at a time, so no tile waits on an index load. The row groups are
+//    summed by the ordered reduce kernel of the gather-axpy.
 // Every sum has a fixed order: results are bitwise reproducible.
 #include <algorithm>
 
