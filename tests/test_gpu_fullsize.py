@@ -6,7 +6,8 @@ pinned on the CPU):
   predicted inline at three density points of the sweep, including every head and neuron;
 * three consecutive decode tokens through two OPT-175B-shaped layers (d 12288, F 49152,
   96 x 128 heads, rank 1000) with the past length held per row in device memory and advanced
-  by the call, against the oracle's own decode (its own scores, sets, outputs and caches).
+  by the call, against the oracle's own decode (its own scores, sets, outputs and caches);
+  the same at B = 8 with ragged lengths on the union path (two tokens, three sampled rows).
 """
 import numpy as np
 import pytest
@@ -164,6 +165,86 @@ def test_opt175b_shape_decode_three_tokens(dv):
             others = np.setdiff1d(np.arange(W175.n_heads), Sh)
             assert not gk[others].any() and not gv[others].any(), "an unselected head wrote its slot (hole)"
             h_or.append(ref["out"])
+    del dev, kcd, vcd, ws
+    torch.cuda.empty_cache()
+
+
+def _row_cache(wd, which, layer, b, heads, t0, appended):
+    """Row b's cache of the given heads [1][len(heads)][t_max][dh] for a batch of wd.batch rows:
+    the seeded past (slots below the row's own start t0), the oracle's own appends, zero
+    elsewhere."""
+    shp = (wd.batch * wd.n_heads, wd.t_max, wd.head_dim)
+    r = synth.rows(wd.key(which, layer), shp, wd.kv_sigma, wd.dtype, b * wd.n_heads + np.asarray(heads))
+    r[:, t0:, :] = 0
+    for j, h in enumerate(heads):
+        for slot, val in appended.get(int(h), {}).items():
+            r[j, slot] = val
+    return r[None]
+
+
+@pytest.mark.timeout(900)
+def test_opt175b_shape_decode_batch8_ragged(dv):
+    """dv_decode_step on two OPT-175B-shaped layers at B = 8, past lengths 256, 512, ..., 2048
+    held per row on the device and advanced by the call, for two consecutive tokens: the union
+    path on the matrix cores with the side-stream lookahead, as the multi-step decode bench
+    runs it. Rows 0, 3 and 7 against the oracle's own decode of that row (its own scores,
+    sets, outputs and caches)."""
+    n, B, tokens = 2, 8, 2
+    starts = [256 * (b + 1) for b in range(B)]
+    wd = W175.with_(batch=B, t_past=max(starts) + tokens)   # t_max = longest start + tokens + 1: no saturation
+    dims = dims_of(wd)
+    dev = [sdev.layer_on_device(W175, l) for l in range(n)]
+    kcd, vcd = [], []
+    for l in range(n):
+        for which, lst in (("k_cache", kcd), ("v_cache", vcd)):
+            c = sdev.kv_on_device(wd, which, l)
+            for b, t0 in enumerate(starts):
+                c[b, :, t0:, :] = 0
+            lst.append(c)
+    t_rows = torch.tensor(starts, dtype=torch.int32, device="cuda")
+    ws = dv.stack_workspace(dims, B, W175.k, W175.kh)
+    side = torch.cuda.Stream()
+    preds = [predictor_host(W175, l) for l in range(n)]
+    rows = (0, 3, 7)
+    appended = {(b, l, which): {} for b in rows for l in range(n) for which in ("k_cache", "v_cache")}
+    for s in range(tokens):
+        x = synth.x_input(wd, step=300 + s)
+        xd = torch.from_numpy(x).cuda()
+        y = torch.empty_like(xd)
+        h_all = torch.empty(n + 1, B, W175.d_model, device="cuda")
+        io = torch.empty(n, B, W175.k, dtype=torch.int32, device="cuda")
+        ho = torch.empty(n, B, W175.kh, dtype=torch.int32, device="cuda")
+        dv.dv_decode_step(dims, [layer_weights(t) for t in dev], [pred_weights(t) for t in dev], xd, W175.k, W175.kh,
+                          kcd, vcd, t_rows, y, advance=True, h_all=h_all, idx_out=io, heads_out=ho, ws=ws,
+                          side_stream=side)
+        torch.cuda.synchronize()
+        assert t_rows.cpu().tolist() == [t0 + s + 1 for t0 in starts]
+        h = h_all.cpu().numpy()
+        S_all, Sh_all = io.cpu().numpy(), ho.cpu().numpy()
+        for b in rows:
+            T = starts[b] + s
+            h_or = [x[b].astype(np.float64)[None]]
+            for l in range(n):
+                p = preds[l]
+                rm, rh = oracle.predict(p["p1_mlp"], p["p2_mlp"], p["p1_head"], p["p2_head"], h_or[max(l - 1, 0)])
+                S = chosen_sets(S_all[l][b:b + 1], rm, W175.k, f"token {s} row {b} layer {l} neuron set")[0]
+                Sh = chosen_sets(Sh_all[l][b:b + 1], rh, W175.kh, f"token {s} row {b} layer {l} head set")[0]
+                tw = _compact_weights(W175, l, S, Sh)
+                kc = _row_cache(wd, "k_cache", l, b, Sh, starts[b], appended[(b, l, "k_cache")])
+                vc = _row_cache(wd, "v_cache", l, b, Sh, starts[b], appended[(b, l, "v_cache")])
+                ref = oracle.layer(h_or[l], tw, kc, vc, T, [np.arange(len(S))], [np.arange(len(Sh))])
+                assert_close(h[l + 1][b:b + 1], ref["out"], W175.dtype, f"token {s} row {b} (T={T}) layer {l}",
+                             batch=B, depth=l + 1 + s)
+                gk = kcd[l][b, :, T].float().cpu().numpy()
+                gv = vcd[l][b, :, T].float().cpu().numpy()
+                for j, hd in enumerate(Sh):
+                    rk, rv = ref["qkv"][0, j, 1], ref["qkv"][0, j, 2]
+                    assert appended_ok(gk[hd], rk) and appended_ok(gv[hd], rv), f"token {s} row {b} head {hd} k/v"
+                    appended[(b, l, "k_cache")].setdefault(int(hd), {})[T] = rk.astype(np.float16)
+                    appended[(b, l, "v_cache")].setdefault(int(hd), {})[T] = rv.astype(np.float16)
+                others = np.setdiff1d(np.arange(W175.n_heads), Sh)
+                assert not gk[others].any() and not gv[others].any(), f"row {b}: an unselected head wrote its slot"
+                h_or.append(ref["out"])
     del dev, kcd, vcd, ws
     torch.cuda.empty_cache()
 
