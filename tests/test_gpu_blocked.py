@@ -85,3 +85,34 @@ def test_blocked_chain_scores_to_mlp(dv):
     S = oracle.expand_blocks(ref_blocks, bs)
     ref = oracle.mlp(xn, t["w1t"], t["b1"], t["w2"], t["b2"], oracle.masks_from_sets(S, w.d_ffn))["y_m"]
     assert_close(y.cpu().numpy(), ref, w.dtype, "blocked chain y_m")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("bs", [32, 64])
+def test_blocked_mlp_opt175b_shape(dv, bs):
+    """The blocked MLP at the OPT-175B shape the blocked bench times (d 12288, F 49152, 5 % of
+    the neurons as 77 blocks of 32 or 38 blocks of 64), batch 1: y_m against the oracle on the
+    regenerated rows of the selected blocks."""
+    import synth.device as sdev
+    w = synth.OPT175B_STACK
+    F = w.d_ffn
+    kb = (w.k + bs // 2) // bs
+    rng = np.random.default_rng(100 + bs)
+    blocks = np.sort(rng.choice(F // bs, kb, replace=False)).astype(np.int32)[None]
+    xn = rng.standard_normal((1, w.d_model)).astype(np.float32)
+    t = sdev.layer_on_device(w, 0)
+    dims = dims_of(w)
+    y = torch.empty(1, w.d_model, device="cuda")
+    dv.dv_sparse_mlp_blocked(dims, layer_weights(t), torch.from_numpy(xn).cuda(), torch.from_numpy(blocks).cuda(), kb,
+                             bs, y, dv.workspace(dims, 1, kb * bs, 0))
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    del t
+    torch.cuda.empty_cache()
+    S = oracle.expand_blocks(blocks, bs)[0]
+    shapes = synth.layer_shapes(w)
+    rows = {n: synth.rows(w.key(n, 0), *shapes[n], S) for n in ("w1t", "b1", "w2")}
+    b2 = synth.tensor(w.key("b2", 0), *shapes["b2"])
+    ref = oracle.mlp(xn, rows["w1t"], rows["b1"], rows["w2"], b2, np.ones((1, len(S))))["y_m"]
+    assert_close(got, ref, w.dtype, f"OPT-175B-shaped blocked y_m bs={bs}")
+
